@@ -1,0 +1,204 @@
+"""Benchmark of the KDA state-recurrence hot path on one MI355X.
+
+One step = one pass of the whole path over resident synthetic inputs:
+  * kda_chunk_prefill on the single-layer workload (1 sequence, T = 8229 =
+    128 full chunks + a tail of 37, H = 32 heads, d_k = d_v = 128, chunk 64,
+    bf16 q/k/v/g/b, fp32 pool, zero initial state, snapshot at c = 128);
+  * kda_recurrent_verify, kda_commit and kda_state_copy on the speculative
+    workload (256 requests, L = 8, H = 32, fp32 128 x 128 checkpoints in a
+    1024-slot pool, accepted ~ U{0..8}, in-place commit, fork of 64
+    committed checkpoints to 4 children each).
+value = prefill tokens/s (T / mean prefill time).  Each call is bracketed by
+HIP events on the stream it is launched on; the roofline object covers the
+call that dominates the step.  The cpu_baseline leg times the fp64 oracle
+(single thread) on the first tokens of the same prefill workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import linear_attention_state_kda_amd as kda  # noqa: E402
+import workloads as wl  # noqa: E402
+
+HBM_PEAK = 8.0e12            # bytes/s, MI355X HBM3E
+BF16_PEAK = 2.5e15           # FLOP/s, dense bf16 MFMA
+METRIC = "KDA chunk-prefill tokens/s + %MFMA peak; verify/commit state GB/s + %HBM"
+
+
+def i32(x, dev):
+    return torch.as_tensor(np.asarray(x, dtype=np.int32), device=dev)
+
+
+def prefill_setup(dev):
+    case = wl.single_layer_prefill()
+    toks, cu = wl.prefill_tokens(case)
+    H, d, C = case["H"], case["dk"], case["chunk"]
+    t = {n: toks[n].to(dev) for n in "qkvgb"}
+    pool = torch.zeros((case["n_slots"], H, d, d), dtype=torch.float32, device=dev)
+    s, c, slot = case["tracks"][0]
+    args = dict(q=t["q"], k=t["k"], v=t["v"], g=t["g"], b=t["b"], cu_seqlens=i32(cu, dev), chunk=C,
+                pool=pool, init_slot=i32(case["init_slots"], dev), final_slot=i32(case["final_slots"], dev),
+                track_ptr=i32([0, 1], dev), track_chunk=i32([c], dev), track_slot=i32([slot], dev),
+                track_f32=torch.empty((1, H, d, d), dtype=torch.float32, device=dev))
+    T = int(cu[-1])
+    args["o"] = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+    args["workspace"] = torch.empty(kda.prefill_workspace_bytes(1, T, H, d, d, C, torch.bfloat16),
+                                    dtype=torch.uint8, device=dev)
+    # algorithmic traffic and work: per token-head 4d+1 inputs
+    # and d outputs in bf16; per sequence-head the zero init reads nothing, the
+    # final state and one snapshot are written in fp32 plus the fp32 copy.
+    bytes_ = T * H * (4 * d * 2 + 2 + d * 2) + H * d * d * 4 * 3
+    flops = T * H * (6 * d * d + 5 * C * d)
+    return case, args, T, bytes_, flops
+
+
+def spec_setup(dev):
+    case = wl.spec_case(seed=3)
+    n_req, L, H, d = case["n_req"], case["L"], case["H"], case["dk"]
+    toks = wl.token_inputs(n_req * L, H, d, d, "bf16", case["seed"], shape_prefix=(n_req, L))
+    t = {n: toks[n].to(dev) for n in "qkvgb"}
+    pool = torch.zeros((case["n_slots"], H, d, d), dtype=torch.float32, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(case["seed"])
+    ck = torch.as_tensor(case["ckpt_slots"], dtype=torch.long, device=dev)
+    pool[ck] = torch.randn((n_req, H, d, d), generator=gen, device=dev)
+    o = torch.empty((n_req, L, H, d), dtype=torch.bfloat16, device=dev)
+    u_rec = torch.empty((n_req, H, L, d), dtype=torch.float32, device=dev)
+    kg_rec = torch.empty((n_req, H, L, 2 * d), dtype=torch.bfloat16, device=dev)
+    acc = case["accepted"]
+    s_in = 2
+    verify_bytes = n_req * H * (d * d * 4 + L * (4 * d * s_in + s_in + d * s_in + 4 * d + 2 * d * s_in))
+    commit_bytes = sum(H * (2 * d * d * 4 + int(n) * (4 * d + 2 * d * s_in)) for n in acc if n > 0)
+    copy_bytes = len(case["fork_src"]) * 2 * H * d * d * 4
+    return dict(case=case, t=t, pool=pool, o=o, u_rec=u_rec, kg_rec=kg_rec,
+                ckpt=i32(case["ckpt_slots"], dev), acc=i32(acc, dev),
+                src=i32(case["fork_src"], dev), dst=i32(case["fork_dst"], dev),
+                bytes=dict(verify=verify_bytes, commit=commit_bytes, copy=copy_bytes))
+
+
+def cpu_baseline(case, seconds_target=10.0):
+    """Time the fp64 oracle, single thread, on the first tokens of the prefill."""
+    from threadpoolctl import threadpool_limits
+    from oracle import kda_oracle as ko
+
+    toks, _ = wl.prefill_tokens(case)
+    H, d = case["H"], case["dk"]
+    ex = {n: wl.exact(toks[n]) for n in "qkvgb"}
+    with threadpool_limits(limits=1):
+        n = 64
+        t0 = time.perf_counter()
+        ko.run_sequence(*(ex[x][:n] for x in "qkvgb"), np.zeros((H, d, d)))
+        per_tok = (time.perf_counter() - t0) / n
+        n2 = int(max(256, min(case["lengths"][0], seconds_target / per_tok)))
+        t0 = time.perf_counter()
+        ko.run_sequence(*(ex[x][:n2] for x in "qkvgb"), np.zeros((H, d, d)))
+        dt = time.perf_counter() - t0
+    return {"value": n2 / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n2} of {case['lengths'][0]} tokens of the single-layer prefill, all "
+                      f"{H} heads, fp64 token loop ({dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the KDA path here is built and timed on a single "
+              "MI355X (no collectives); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    kda.lib()
+    case, pargs, T, p_bytes, p_flops = prefill_setup(dev)
+    sp = spec_setup(dev)
+    st = torch.cuda.current_stream()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    calls = ["prefill", "verify", "commit", "copy"]
+
+    def step(events=None):
+        def mark(i):
+            if events is not None:
+                events[i].record(st)
+        mark(0)
+        kda.chunk_prefill(**pargs)
+        mark(1)
+        t = sp["t"]
+        kda.recurrent_verify(t["q"], t["k"], t["v"], t["g"], t["b"], sp["pool"], sp["ckpt"],
+                             o=sp["o"], u_rec=sp["u_rec"], kg_rec=sp["kg_rec"])
+        mark(2)
+        kda.commit(sp["pool"], sp["ckpt"], sp["acc"], sp["u_rec"], sp["kg_rec"])
+        mark(3)
+        kda.state_copy(sp["pool"], sp["src"], sp["dst"])
+        mark(4)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[ev() for _ in range(5)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(a.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {c: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(a.steps)]))
+          for i, c in enumerate(calls)}
+    ms_step = wall / a.steps * 1e3
+
+    p_s = ms["prefill"] * 1e-3
+    tokens_per_s = T / p_s
+    gbs = {c: sp["bytes"][c] / (ms[c] * 1e-3) / 1e9 for c in ("verify", "commit", "copy")}
+    dominant = max(calls, key=lambda c: ms[c])
+    if dominant == "prefill":
+        achieved = p_bytes / p_s / 1e9
+        roof = {"kernel": "kda_chunk_prefill (kda_chunk_map + kda_chunk_prep + kda_chunk_scan)",
+                "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                "frac": achieved * 1e9 / HBM_PEAK, "traffic": None,
+                "algorithmic_bytes_per_launch": p_bytes, "avg_launch_ms": ms["prefill"]}
+    else:
+        achieved = gbs[dominant]
+        roof = {"kernel": f"kda_{dominant}", "bound": "hbm", "achieved": achieved,
+                "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": achieved * 1e9 / HBM_PEAK,
+                "traffic": None, "algorithmic_bytes_per_launch": sp["bytes"][dominant],
+                "avg_launch_ms": ms[dominant]}
+    out = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "single-layer KDA prefill T=8229 H=32 d_k=d_v=128 chunk=64 bf16 "
+                               "fp32-pool + spec-decode verify/commit/fork n_req=256 L=8 H=32",
+                   "global_batch": 1, "seq_len": T, "heads": 32, "head_dim": 128, "chunk": 64},
+        "prefill": {"ms": ms["prefill"], "tokens_per_s": tokens_per_s,
+                    "hbm_GBps": p_bytes / p_s / 1e9, "hbm_frac": p_bytes / p_s / HBM_PEAK,
+                    "mfma_TFLOPs": p_flops / p_s / 1e12, "mfma_frac": p_flops / p_s / BF16_PEAK},
+        "verify": {"ms": ms["verify"], "GBps": gbs["verify"], "hbm_frac": gbs["verify"] * 1e9 / HBM_PEAK},
+        "commit": {"ms": ms["commit"], "GBps": gbs["commit"], "hbm_frac": gbs["commit"] * 1e9 / HBM_PEAK},
+        "copy": {"ms": ms["copy"], "GBps": gbs["copy"], "hbm_frac": gbs["copy"] * 1e9 / HBM_PEAK},
+        "roofline": roof,
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not a.no_cpu_baseline:
+        cb = cpu_baseline(case)
+        cb["cpu"] = platform.processor() or platform.machine()
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

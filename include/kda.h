@@ -1,0 +1,179 @@
+/*
+ * kda.h - C ABI of the MI355X (gfx950) KDA state-recurrence library, libkda.so.
+ *
+ * The library implements the hot path of Kimi Delta Attention's recurrent
+ * state as four GPU calls.  Per head the state S is a d_k x d_v fp32 matrix
+ * and one token does
+ *
+ *     alpha = exp(g)      (g = log alpha, one value per key channel)
+ *     beta  = sigmoid(b)  (b = beta logit, one value per head)
+ *     u     = beta * (v - (Diag(alpha) S)^T k)
+ *     S     = Diag(alpha) S + k u^T
+ *     o     = S^T q
+ *
+ * Sources, by page title and section (the pages give structure, not code):
+ *  [P1] "State semantics deep water: rollback, fork, replay consistency, TP
+ *       state": sec. 1 (fixed-size per-head state), sec. 2 (rollback is an
+ *       exact block copy), sec. 3 (fork copies the whole state, COW off),
+ *       sec. 4 (sigmoid beta; chunk vs recurrent activation placement).
+ *  [P2] SGLang PR #34820 summary: "Implementation breakdown" items 1-4 and the
+ *       kda_backend.py / hybrid_linear_attn_backend.py / kda_prefill.py
+ *       excerpts (fp32 track snapshot at a chunk index, one cast into the
+ *       pool dtype, sync-free indexed copies, explicit error instead of a
+ *       silently unwritten snapshot).
+ *  [P3] vLLM PR #51855 summary: "Implementation breakdown" steps 1-5 (one
+ *       checkpoint; fp32 correction u and key/raw-gate records; reverse-order
+ *       non-recursive commit) and "Risks" item 1 (reject at call time what a
+ *       kernel would otherwise trip over at run time).
+ *
+ * Conventions shared by every call
+ *  - Every pointer except `stream` and the pool struct itself is a DEVICE
+ *    pointer.  The caller owns all buffers; the library keeps no pointer
+ *    after a call returns and holds no global mutable state.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream).  No call reads device memory back to the host, none allocates,
+ *    and none synchronises, so all of them can be captured in a HIP graph.
+ *  - Every condition checkable on the host (null pointers, negative counts,
+ *    unsupported shapes or dtypes, a workspace that is too small) returns a
+ *    non-zero kda_status before any launch and touches no device memory.
+ *  - Conditions only the device can see (a slot index out of range, a
+ *    snapshot chunk outside its sequence, accepted length outside [0, L],
+ *    malformed cu_seqlens or track_ptr) set a bit in *dev_err (when dev_err
+ *    is non-NULL, via atomic OR) and the offending item is skipped.  The
+ *    caller clears *dev_err before the call if it wants a fresh word.
+ *  - Every cast into a 16-bit output or pool is one round-to-nearest-even
+ *    cast from an fp32 value held in registers.
+ *  - Floating-point results are deterministic run to run.
+ *
+ * Layouts (row-major, innermost last):
+ *  tokens (prefill):   q, k, g [T_total][H][d_k];  v, o [T_total][H][d_v];
+ *                      b [T_total][H]
+ *  speculative (verify): q, k, g [n_req][L][H][d_k]; v, o [n_req][L][H][d_v];
+ *                      b [n_req][L][H]
+ *  state pool:         [n_slots][H][d_v][d_k]  (per head, row v holds the
+ *                      d_k entries S[0..d_k-1][v]; k is contiguous)
+ *  records:            u_rec [n_req][H][L][d_v] fp32;
+ *                      kg_rec [n_req][H][L][2*d_k]: key then raw gate g
+ *
+ * Built shapes: (d_k, d_v, chunk) = (128, 128, 64) with bf16 or fp16 inputs,
+ * and (16, 16, 16) with fp32 inputs.  Pools may be fp32, fp16 or bf16.  The
+ * verify, commit and copy calls accept d_k = d_v in {16, 32, 64, 128}.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARG = 1, /* null pointer, negative count, inconsistent sizes */
+  KDA_ERR_UNSUPPORTED = 2, /* shape / dtype combination that is not built      */
+  KDA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required       */
+  KDA_ERR_LAUNCH = 4       /* the HIP runtime rejected a kernel launch         */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_F16 = 1, KDA_BF16 = 2 } kda_dtype;
+
+/* Bits set in *dev_err by the kernels. */
+#define KDA_DEV_ERR_SLOT 1u   /* a slot index outside [0, n_slots) (or -1 where not allowed) */
+#define KDA_DEV_ERR_TRACK 2u  /* a snapshot chunk outside [0, floor(T_i / chunk)], or a bad track_ptr */
+#define KDA_DEV_ERR_ACCEPT 4u /* an accepted length outside [0, L] */
+#define KDA_DEV_ERR_SEQLEN 8u /* cu_seqlens decreasing, negative, or beyond total_tokens */
+
+/* A slot-indexed state pool, passed by value.  base points to
+ * n_slots * H * d_v * d_k elements of `dtype` (a kda_dtype value). */
+typedef struct {
+  void* base;
+  int64_t n_slots;
+  int32_t dtype;
+  int32_t H;
+  int32_t d_k;
+  int32_t d_v;
+} kda_pool;
+
+/* Bytes of device workspace kda_chunk_prefill needs for these sizes
+ * (an upper bound that depends only on the arguments).  *bytes is set on
+ * KDA_OK.  Same shape checks as kda_chunk_prefill. */
+kda_status kda_chunk_prefill_workspace(int32_t n_seqs, int64_t total_tokens, int32_t H,
+                                       int32_t d_k, int32_t d_v, int32_t chunk,
+                                       int32_t in_dtype, size_t* bytes);
+
+/* Chunked prefill over packed variable-length sequences ([P2] items 1-2 and
+ * the kda_prefill.py excerpt; serial steps = ceil(T_i / chunk), [P1] sec. 5).
+ *
+ * q, k, v, g, b   inputs in `in_dtype` (layouts above); o output, same dtype.
+ * cu_seqlens      int32 [n_seqs + 1] token offsets, non-decreasing, last <= total_tokens.
+ * pool            state pool; pool.H, d_k, d_v must equal H, d_k, d_v.
+ * init_slot       int32 [n_seqs]: slot holding the initial state of sequence
+ *                 i (upcast exactly to fp32), or -1 for a zero state.
+ * final_slot      int32 [n_seqs]: slot that receives the final state (one
+ *                 RNE cast), or -1 for none.  It may equal the sequence's own
+ *                 init_slot; every other written slot must be distinct from
+ *                 every slot read or written in the call.
+ * track_ptr       int32 [n_seqs + 1] CSR offsets into track_chunk/track_slot
+ *                 (may be NULL when n_track == 0).  Entry e of sequence i asks
+ *                 for the state after track_chunk[e] full chunks of that
+ *                 sequence, 0 <= track_chunk[e] <= floor(T_i / chunk): taken
+ *                 straight from the fp32 accumulator, written to
+ *                 track_f32[e] (fp32 [n_track][H][d_v][d_k], optional) and,
+ *                 unless track_slot[e] == -1, cast once into that pool slot.
+ * dev_err         optional device word for the KDA_DEV_ERR_* bits.
+ * workspace       device scratch of at least kda_chunk_prefill_workspace()
+ *                 bytes, 256-byte aligned; its contents need no initialisation.
+ */
+kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const void* g,
+                             const void* b, int32_t in_dtype, void* o,
+                             const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens,
+                             int32_t H, int32_t d_k, int32_t d_v, int32_t chunk, kda_pool pool,
+                             const int32_t* init_slot, const int32_t* final_slot,
+                             const int32_t* track_ptr, const int32_t* track_chunk,
+                             const int32_t* track_slot, int32_t n_track, float* track_f32,
+                             int32_t* dev_err, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Speculative-decode verify ([P3] step 3): per request, read the checkpoint
+ * in pool slot ckpt_slot[r] (never written), step the L positions token by
+ * token with the gate activations applied inside the kernel, and write
+ *   o       [n_req][L][H][d_v] in in_dtype,
+ *   u_rec   [n_req][H][L][d_v] fp32 correction u_t (beta folded in),
+ *   kg_rec  [n_req][H][L][2*d_k] in in_dtype: key k_t then raw gate g_t.
+ * 1 <= L <= 256. */
+kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, const void* g,
+                                const void* b, int32_t in_dtype, void* o, int32_t n_req,
+                                int32_t L, int32_t H, int32_t d_k, int32_t d_v, kda_pool pool,
+                                const int32_t* ckpt_slot, float* u_rec, void* kg_rec,
+                                int32_t* dev_err, void* stream);
+
+/* RecoverSSM commit ([P3] step 4): rebuild, without re-running the
+ * recurrence, the state after accepted_len[r] = n positions,
+ *   S_n = Diag(e^{sum_{t<=n} g_t}) S_0 + sum_{t<=n} Diag(e^{sum_{t<s<=n} g_s}) k_t u_t^T,
+ * accumulated in reverse order t = n..1, from the checkpoint in
+ * ckpt_slot[r] and the records of a verify call; write it (one RNE cast) to
+ * dst_slot[r] (dst_slot == NULL means in place, dst_slot[r] == ckpt_slot[r]
+ * is allowed).  An in-place request with n == 0 touches nothing.  rec_dtype
+ * is the dtype of kg_rec.  0 <= accepted_len[r] <= L <= 256. */
+kda_status kda_commit(kda_pool pool, const int32_t* ckpt_slot, const int32_t* dst_slot,
+                      const int32_t* accepted_len, const float* u_rec, const void* kg_rec,
+                      int32_t rec_dtype, int32_t n_req, int32_t L, int32_t H, int32_t d_k,
+                      int32_t d_v, int32_t* dev_err, void* stream);
+
+/* Rollback / fork ([P1] secs. 2-3; one launch for many slots as in the
+ * fused slot copy of sec. 2): for every pair i, pool slot dst_slot[i]
+ * receives the bits of slot src_slot[i].  Destinations must be distinct and
+ * disjoint from the sources; src == dst is a no-op. */
+kda_status kda_state_copy(kda_pool pool, const int32_t* src_slot, const int32_t* dst_slot,
+                          int32_t n_pairs, int32_t* dev_err, void* stream);
+
+/* Static, NUL-terminated name of a status code. */
+const char* kda_status_string(kda_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

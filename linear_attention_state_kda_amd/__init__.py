@@ -1,0 +1,199 @@
+"""Thin Python binding of libkda.so, the MI355X KDA state-recurrence library.
+
+Argument marshalling only: every step of the recurrence runs in the HIP
+kernels behind the C ABI declared in ``include/kda.h``.  PyTorch provides
+device memory and the current stream.  The functions carry the C names
+without the ``kda_`` prefix and raise ``KdaError`` on a non-zero status.
+There is no fallback: if the library is not built, loading it raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "KdaError", "lib", "DTYPE_CODES", "DEV_ERR_SLOT", "DEV_ERR_TRACK", "DEV_ERR_ACCEPT",
+    "DEV_ERR_SEQLEN", "prefill_workspace_bytes", "chunk_prefill", "recurrent_verify",
+    "commit", "state_copy", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+
+DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED",
+          3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_LAUNCH"}
+DEV_ERR_SLOT, DEV_ERR_TRACK, DEV_ERR_ACCEPT, DEV_ERR_SEQLEN = 1, 2, 4, 8
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = int(status)
+        super().__init__(f"{where}: {STATUS.get(self.status, self.status)}")
+
+
+class KdaPool(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("n_slots", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+
+_SIGS = {
+    "kda_chunk_prefill_workspace": [_I32, _I64, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)],
+    "kda_chunk_prefill": [_P, _P, _P, _P, _P, _I32, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32,
+                          KdaPool, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P],
+    "kda_recurrent_verify": [_P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, KdaPool,
+                             _P, _P, _P, _P, _P],
+    "kda_commit": [KdaPool, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P],
+    "kda_state_copy": [KdaPool, _P, _P, _I32, _P, _P],
+    "kda_status_string": [_I32],
+}
+
+_lib = None
+
+
+def lib():
+    """Load libkda.so (built in-tree by ``linear_attention_state_kda_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise KdaError(-1, f"libkda.so not built at {LIB_PATH}; run linear_attention_state_kda_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_char_p if name == "kda_status_string" else ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name, dtype=None, ndim=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _pool(pool):
+    _dev(pool, "pool", ndim=4)
+    if pool.dtype not in DTYPE_CODES:
+        raise ValueError("pool dtype must be float32, float16 or bfloat16")
+    n, H, dv, dk = pool.shape
+    return KdaPool(pool.data_ptr(), n, DTYPE_CODES[pool.dtype], H, dk, dv)
+
+
+def _check(status, where):
+    if status != 0:
+        raise KdaError(status, where)
+
+
+def prefill_workspace_bytes(n_seqs, total_tokens, H, d_k, d_v, chunk, in_dtype):
+    out = _SZ(0)
+    _check(lib().kda_chunk_prefill_workspace(n_seqs, total_tokens, H, d_k, d_v, chunk,
+                                             DTYPE_CODES[in_dtype], ctypes.byref(out)),
+           "kda_chunk_prefill_workspace")
+    return int(out.value)
+
+
+def chunk_prefill(q, k, v, g, b, cu_seqlens, chunk, pool, init_slot, final_slot,
+                  track_ptr=None, track_chunk=None, track_slot=None, track_f32=None,
+                  o=None, dev_err=None, workspace=None):
+    """kda_chunk_prefill on packed token tensors q, k, g [T, H, d_k], v [T, H, d_v],
+    b [T, H]; returns o [T, H, d_v] (allocated when not given)."""
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("b", b)):
+        _dev(t, name, dtype=q.dtype)
+    for name, t in (("cu_seqlens", cu_seqlens), ("init_slot", init_slot), ("final_slot", final_slot),
+                    ("track_ptr", track_ptr), ("track_chunk", track_chunk), ("track_slot", track_slot),
+                    ("dev_err", dev_err)):
+        _dev(t, name, dtype=torch.int32)
+    _dev(track_f32, "track_f32", dtype=torch.float32)
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+    _dev(o, "o", dtype=q.dtype)
+    n_seqs = cu_seqlens.numel() - 1
+    n_track = 0 if track_chunk is None else track_chunk.numel()
+    need = prefill_workspace_bytes(n_seqs, T, H, dk, dv, chunk, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace", dtype=torch.uint8)
+    st = lib().kda_chunk_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), DTYPE_CODES[q.dtype], _ptr(o),
+        _ptr(cu_seqlens), n_seqs, T, H, dk, dv, chunk, _pool(pool), _ptr(init_slot),
+        _ptr(final_slot), _ptr(track_ptr), _ptr(track_chunk), _ptr(track_slot), n_track,
+        _ptr(track_f32), _ptr(dev_err), _ptr(workspace), workspace.numel(), _stream())
+    _check(st, "kda_chunk_prefill")
+    return o
+
+
+def recurrent_verify(q, k, v, g, b, pool, ckpt_slot, o=None, u_rec=None, kg_rec=None, dev_err=None):
+    """kda_recurrent_verify on q, k, g [n_req, L, H, d_k], v [n_req, L, H, d_v],
+    b [n_req, L, H]; returns (o, u_rec, kg_rec)."""
+    n_req, L, H, dk = q.shape
+    dv = v.shape[3]
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("b", b)):
+        _dev(t, name, dtype=q.dtype)
+    _dev(ckpt_slot, "ckpt_slot", dtype=torch.int32)
+    _dev(dev_err, "dev_err", dtype=torch.int32)
+    if o is None:
+        o = torch.empty((n_req, L, H, dv), dtype=q.dtype, device=q.device)
+    if u_rec is None:
+        u_rec = torch.empty((n_req, H, L, dv), dtype=torch.float32, device=q.device)
+    if kg_rec is None:
+        kg_rec = torch.empty((n_req, H, L, 2 * dk), dtype=q.dtype, device=q.device)
+    _dev(o, "o", dtype=q.dtype)
+    _dev(u_rec, "u_rec", dtype=torch.float32)
+    _dev(kg_rec, "kg_rec", dtype=q.dtype)
+    st = lib().kda_recurrent_verify(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), DTYPE_CODES[q.dtype], _ptr(o), n_req, L, H,
+        dk, dv, _pool(pool), _ptr(ckpt_slot), _ptr(u_rec), _ptr(kg_rec), _ptr(dev_err), _stream())
+    _check(st, "kda_recurrent_verify")
+    return o, u_rec, kg_rec
+
+
+def commit(pool, ckpt_slot, accepted_len, u_rec, kg_rec, dst_slot=None, dev_err=None):
+    """kda_commit: rebuild each request's state at its accepted length."""
+    n_req, H, L, dv = u_rec.shape
+    dk = kg_rec.shape[3] // 2
+    for name, t in (("ckpt_slot", ckpt_slot), ("accepted_len", accepted_len), ("dst_slot", dst_slot),
+                    ("dev_err", dev_err)):
+        _dev(t, name, dtype=torch.int32)
+    _dev(u_rec, "u_rec", dtype=torch.float32)
+    _dev(kg_rec, "kg_rec")
+    st = lib().kda_commit(_pool(pool), _ptr(ckpt_slot), _ptr(dst_slot), _ptr(accepted_len),
+                          _ptr(u_rec), _ptr(kg_rec), DTYPE_CODES[kg_rec.dtype], n_req, L, H, dk,
+                          dv, _ptr(dev_err), _stream())
+    _check(st, "kda_commit")
+
+
+def state_copy(pool, src_slot, dst_slot, dev_err=None):
+    """kda_state_copy: pool[dst_slot[i]] <- pool[src_slot[i]] bitwise."""
+    _dev(src_slot, "src_slot", dtype=torch.int32)
+    _dev(dst_slot, "dst_slot", dtype=torch.int32)
+    _dev(dev_err, "dev_err", dtype=torch.int32)
+    if src_slot.numel() != dst_slot.numel():
+        raise ValueError("src_slot and dst_slot differ in length")
+    st = lib().kda_state_copy(_pool(pool), _ptr(src_slot), _ptr(dst_slot), src_slot.numel(),
+                              _ptr(dev_err), _stream())
+    _check(st, "kda_state_copy")

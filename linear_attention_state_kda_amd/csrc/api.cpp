@@ -1,0 +1,149 @@
+// C ABI of libkda.so: host-side validation, then one asynchronous launch
+// sequence on the caller's stream.  Everything checkable on the host is
+// rejected here, before any device memory is touched (vLLM PR #51855 summary,
+// risks item 1: a configuration the kernel cannot serve must fail at call
+// time, not inside the first step that hits it).
+#include <hip/hip_runtime.h>
+
+#include "../../include/kda.h"
+#include "kda_launch.hpp"
+
+namespace {
+
+bool dtype_ok(int32_t dt) { return dt == KDA_F32 || dt == KDA_F16 || dt == KDA_BF16; }
+
+size_t dtype_size(int32_t dt) { return dt == KDA_F32 ? 4 : 2; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+kda::PoolDesc pool_desc(const kda_pool& p) { return kda::PoolDesc{p.base, p.n_slots, p.dtype}; }
+
+kda_status check_pool(const kda_pool& p, int32_t H, int32_t dk, int32_t dv) {
+  if (p.base == nullptr || p.n_slots <= 0) return KDA_ERR_INVALID_ARG;
+  if (!dtype_ok(p.dtype)) return KDA_ERR_UNSUPPORTED;
+  if (!aligned(p.base, 16)) return KDA_ERR_INVALID_ARG;
+  if (p.H != H || p.d_k != dk || p.d_v != dv) return KDA_ERR_INVALID_ARG;
+  return KDA_OK;
+}
+
+kda_status launched(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+    case KDA_ERR_LAUNCH: return "KDA_ERR_LAUNCH";
+  }
+  return "KDA_ERR_UNKNOWN";
+}
+
+kda_status kda_chunk_prefill_workspace(int32_t n_seqs, int64_t total_tokens, int32_t H,
+                                       int32_t d_k, int32_t d_v, int32_t chunk, int32_t in_dtype,
+                                       size_t* bytes) {
+  if (bytes == nullptr || n_seqs < 0 || total_tokens < 0 || H <= 0) return KDA_ERR_INVALID_ARG;
+  if (!dtype_ok(in_dtype)) return KDA_ERR_UNSUPPORTED;
+  if (!kda::prefill_supported(d_k, d_v, chunk, in_dtype, KDA_F32)) return KDA_ERR_UNSUPPORTED;
+  if (total_tokens > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  *bytes = kda::prefill_workspace_bytes(n_seqs, total_tokens, H, d_k, d_v, chunk, in_dtype);
+  return KDA_OK;
+}
+
+kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const void* g,
+                             const void* b, int32_t in_dtype, void* o,
+                             const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens,
+                             int32_t H, int32_t d_k, int32_t d_v, int32_t chunk, kda_pool pool,
+                             const int32_t* init_slot, const int32_t* final_slot,
+                             const int32_t* track_ptr, const int32_t* track_chunk,
+                             const int32_t* track_slot, int32_t n_track, float* track_f32,
+                             int32_t* dev_err, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (n_seqs < 0 || total_tokens < 0 || H <= 0 || n_track < 0) return KDA_ERR_INVALID_ARG;
+  if (!dtype_ok(in_dtype)) return KDA_ERR_UNSUPPORTED;
+  if (!kda::prefill_supported(d_k, d_v, chunk, in_dtype, pool.dtype)) return KDA_ERR_UNSUPPORTED;
+  if (total_tokens > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  kda_status ps = check_pool(pool, H, d_k, d_v);
+  if (ps != KDA_OK) return ps;
+  if (n_seqs == 0) return KDA_OK;
+  if (cu_seqlens == nullptr || init_slot == nullptr || final_slot == nullptr) return KDA_ERR_INVALID_ARG;
+  if (total_tokens > 0 && (q == nullptr || k == nullptr || v == nullptr || g == nullptr ||
+                           b == nullptr || o == nullptr))
+    return KDA_ERR_INVALID_ARG;
+  if (n_track > 0 && (track_ptr == nullptr || track_chunk == nullptr || track_slot == nullptr))
+    return KDA_ERR_INVALID_ARG;
+  // 4-element vector loads of q, k, g and 16-byte stores of track_f32
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(g, 16) || !aligned(track_f32, 16))
+    return KDA_ERR_INVALID_ARG;
+  const size_t need = kda::prefill_workspace_bytes(n_seqs, total_tokens, H, d_k, d_v, chunk, in_dtype);
+  if (workspace == nullptr || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_WORKSPACE;
+  kda::PrefillArgs a{q, k, v, g, b, o, in_dtype, cu_seqlens, n_seqs, total_tokens, H, d_k, d_v,
+                     chunk, pool_desc(pool), init_slot, final_slot,
+                     n_track > 0 ? track_ptr : nullptr, track_chunk, track_slot, n_track,
+                     track_f32, dev_err, workspace};
+  return launched(kda::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, const void* g,
+                                const void* b, int32_t in_dtype, void* o, int32_t n_req,
+                                int32_t L, int32_t H, int32_t d_k, int32_t d_v, kda_pool pool,
+                                const int32_t* ckpt_slot, float* u_rec, void* kg_rec,
+                                int32_t* dev_err, void* stream) {
+  if (n_req < 0 || H <= 0 || L < 1) return KDA_ERR_INVALID_ARG;
+  if (L > 256) return KDA_ERR_UNSUPPORTED;
+  if (!dtype_ok(in_dtype)) return KDA_ERR_UNSUPPORTED;
+  if (d_k != 128 || d_v != 128) return KDA_ERR_UNSUPPORTED;
+  kda_status ps = check_pool(pool, H, d_k, d_v);
+  if (ps != KDA_OK) return ps;
+  if (n_req == 0) return KDA_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || g == nullptr || b == nullptr ||
+      o == nullptr || ckpt_slot == nullptr || u_rec == nullptr || kg_rec == nullptr)
+    return KDA_ERR_INVALID_ARG;
+  if ((int64_t)n_req * H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  kda::VerifyArgs a{q, k, v, g, b, o, in_dtype, n_req, L, H, d_k, pool_desc(pool), ckpt_slot,
+                    u_rec, kg_rec, dev_err};
+  return launched(kda::launch_verify(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status kda_commit(kda_pool pool, const int32_t* ckpt_slot, const int32_t* dst_slot,
+                      const int32_t* accepted_len, const float* u_rec, const void* kg_rec,
+                      int32_t rec_dtype, int32_t n_req, int32_t L, int32_t H, int32_t d_k,
+                      int32_t d_v, int32_t* dev_err, void* stream) {
+  if (n_req < 0 || H <= 0 || L < 1) return KDA_ERR_INVALID_ARG;
+  if (L > 256) return KDA_ERR_UNSUPPORTED;
+  if (!dtype_ok(rec_dtype)) return KDA_ERR_UNSUPPORTED;
+  if (d_k != 128 || d_v != 128) return KDA_ERR_UNSUPPORTED;
+  kda_status ps = check_pool(pool, H, d_k, d_v);
+  if (ps != KDA_OK) return ps;
+  if (n_req == 0) return KDA_OK;
+  if (ckpt_slot == nullptr || accepted_len == nullptr || u_rec == nullptr || kg_rec == nullptr)
+    return KDA_ERR_INVALID_ARG;
+  if ((int64_t)n_req * H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  kda::CommitArgs a{pool_desc(pool), ckpt_slot, dst_slot, accepted_len, u_rec, kg_rec, rec_dtype,
+                    n_req, L, H, d_k, dev_err};
+  return launched(kda::launch_commit(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status kda_state_copy(kda_pool pool, const int32_t* src_slot, const int32_t* dst_slot,
+                          int32_t n_pairs, int32_t* dev_err, void* stream) {
+  if (n_pairs < 0) return KDA_ERR_INVALID_ARG;
+  if (pool.base == nullptr || pool.n_slots <= 0 || pool.H <= 0 || pool.d_k <= 0 || pool.d_v <= 0)
+    return KDA_ERR_INVALID_ARG;
+  if (!dtype_ok(pool.dtype)) return KDA_ERR_UNSUPPORTED;
+  const int64_t slot_bytes = (int64_t)pool.H * pool.d_k * pool.d_v * (int64_t)dtype_size(pool.dtype);
+  if (slot_bytes % 16 != 0) return KDA_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(pool.base) & 15u) != 0) return KDA_ERR_INVALID_ARG;
+  if (n_pairs == 0) return KDA_OK;
+  if (src_slot == nullptr || dst_slot == nullptr) return KDA_ERR_INVALID_ARG;
+  const int64_t bpp = (slot_bytes + 16383) / 16384;
+  if (bpp * n_pairs > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  kda::CopyArgs a{pool_desc(pool), src_slot, dst_slot, n_pairs, slot_bytes, dev_err};
+  return launched(kda::launch_copy(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Indexed whole-state copy for gfx950: rollback restores the state saved at
+// the verify point and a fork gives each candidate its own copy; both are
+// exact block copies of a fixed-size state (state-semantics page, secs. 2-3).
+// One launch covers every (src, dst) pair, as the fused slot copy of sec. 2
+// does, so many small copies are not launch-bound.
+//
+// Grid: blocks_per_pair consecutive blocks per pair; each thread moves 4 x 16
+// bytes with non-temporal loads issued before the stores.
+#include "kda_common.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+namespace {
+
+constexpr int kT = 256;
+constexpr int kVec = 4;                   // 16-byte vectors per thread per block
+constexpr int64_t kBlockBytes = kT * kVec * 16;
+
+__global__ __launch_bounds__(kT) void kda_copy_kernel(uint8_t* __restrict__ pool, int64_t n_slots,
+                                                      int64_t slot_bytes, int blocks_per_pair,
+                                                      const int32_t* __restrict__ src_slot,
+                                                      const int32_t* __restrict__ dst_slot,
+                                                      int n_pairs, int32_t* __restrict__ dev_err) {
+  const int pair = blockIdx.x / blocks_per_pair;
+  const int part = blockIdx.x % blocks_per_pair;
+  if (pair >= n_pairs) return;
+  const int s = src_slot[pair], d = dst_slot[pair];
+  if (s < 0 || (int64_t)s >= n_slots || d < 0 || (int64_t)d >= n_slots) {
+    if (part == 0 && threadIdx.x == 0) set_err(dev_err, 1u);
+    return;
+  }
+  if (s == d) return;
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4* sp = reinterpret_cast<const u32x4*>(pool + (int64_t)s * slot_bytes);
+  u32x4* dp = reinterpret_cast<u32x4*>(pool + (int64_t)d * slot_bytes);
+  const int64_t n16 = slot_bytes / 16;
+  const int64_t base = (int64_t)part * (kT * kVec) + threadIdx.x;
+  u32x4 buf[kVec];
+#pragma unroll
+  for (int i = 0; i < kVec; ++i) {
+    const int64_t e = base + (int64_t)i * kT;
+    if (e < n16) buf[i] = __builtin_nontemporal_load(sp + e);
+  }
+#pragma unroll
+  for (int i = 0; i < kVec; ++i) {
+    const int64_t e = base + (int64_t)i * kT;
+    if (e < n16) __builtin_nontemporal_store(buf[i], dp + e);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_copy(const CopyArgs& a, hipStream_t st) {
+  if (a.n_pairs == 0) return hipSuccess;
+  const int bpp = (int)((a.slot_bytes + kBlockBytes - 1) / kBlockBytes);
+  const int64_t blocks = (int64_t)bpp * a.n_pairs;
+  hipLaunchKernelGGL(kda_copy_kernel, dim3((unsigned)blocks), dim3(kT), 0, st,
+                     static_cast<uint8_t*>(a.pool.base), a.pool.n_slots, a.slot_bytes, bpp,
+                     a.src_slot, a.dst_slot, a.n_pairs, a.dev_err);
+  return hipGetLastError();
+}
+
+}  // namespace kda

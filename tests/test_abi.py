@@ -1,0 +1,135 @@
+"""Host-side checks of libkda.so (no GPU needed, no kernel launched).
+
+* the library loads and exports exactly the functions include/kda.h declares;
+* status strings;
+* every host-checkable error returns its status before any launch: the
+  pointers passed here are fake addresses that would fault if touched.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import linear_attention_state_kda_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+FAKE = ctypes.c_void_p(0x1000)       # 256-byte aligned, never dereferenced
+FAKE_WS = ctypes.c_void_p(0x100000)
+
+
+def declared():
+    text = open(HEADER).read()
+    return set(re.findall(r"^(?:kda_status|const char\*)\s+(kda_\w+)\s*\(", text, re.M))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kda.LIB_PATH):
+        from linear_attention_state_kda_amd import build
+        build.build()
+    return kda.lib()
+
+
+def test_exports_match_header(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s+(kda_\w+)$", out, re.M))
+    assert declared() == exported, (declared(), exported)
+    for name in declared():
+        assert getattr(L, name) is not None
+
+
+def test_status_strings(L):
+    names = [L.kda_status_string(i).decode() for i in range(5)]
+    assert names == ["KDA_OK", "KDA_ERR_INVALID_ARG", "KDA_ERR_UNSUPPORTED",
+                     "KDA_ERR_WORKSPACE", "KDA_ERR_LAUNCH"]
+
+
+def pool(H=2, dk=128, dv=128, dtype=0, n_slots=8, base=FAKE):
+    return kda.KdaPool(base.value if base is not None else None, n_slots, dtype, H, dk, dv)
+
+
+def prefill(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, in_dtype=2, o=FAKE, cu=FAKE, n_seqs=1,
+             T=100, H=2, dk=128, dv=128, C=64, pool=pool(), init=FAKE, final=FAKE, tptr=None,
+             tchunk=None, tslot=None, n_track=0, tf32=None, err=None, ws=FAKE_WS,
+             ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return L.kda_chunk_prefill(a["q"], a["k"], a["v"], a["g"], a["b"], a["in_dtype"], a["o"],
+                               a["cu"], a["n_seqs"], a["T"], a["H"], a["dk"], a["dv"], a["C"],
+                               a["pool"], a["init"], a["final"], a["tptr"], a["tchunk"], a["tslot"],
+                               a["n_track"], a["tf32"], a["err"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_prefill_host_errors(L):
+    assert prefill(L, q=None) == 1
+    assert prefill(L, cu=None) == 1
+    assert prefill(L, n_seqs=-1) == 1
+    assert prefill(L, H=0) == 1
+    assert prefill(L, dk=64, dv=64) == 2
+    assert prefill(L, C=32) == 2
+    assert prefill(L, in_dtype=0) == 2          # fp32 inputs are built for (16, 16, 16) only
+    assert prefill(L, in_dtype=7) == 2
+    assert prefill(L, pool=pool(dtype=9)) == 2
+    assert prefill(L, pool=pool(H=3)) == 1      # pool shape disagrees with the call
+    assert prefill(L, pool=pool(base=None)) == 1
+    assert prefill(L, n_track=2) == 1           # track arrays missing
+    assert prefill(L, ws_bytes=16) == 3
+    assert prefill(L, ws=None) == 3
+    assert prefill(L, ws=ctypes.c_void_p(0x100010)) == 3   # misaligned workspace
+    assert prefill(L, q=ctypes.c_void_p(0x1002)) == 1       # misaligned input
+    assert prefill(L, T=1 << 33) == 2
+    # nothing to do: returns before touching anything
+    assert prefill(L, n_seqs=0, q=None, cu=None) == 0
+
+
+def test_workspace_query(L):
+    out = ctypes.c_size_t(0)
+    assert L.kda_chunk_prefill_workspace(16, 135168, 32, 128, 128, 64, 2, ctypes.byref(out)) == 0
+    rec = 66304                               # bytes per (chunk, head) record at d=128, C=64, bf16
+    assert out.value == 256 + (135168 // 64 + 16) * 32 * rec
+    assert kda.prefill_workspace_bytes(1, 64, 2, 16, 16, 16, __import__("torch").float32) > 0
+    assert L.kda_chunk_prefill_workspace(1, 64, 2, 32, 32, 16, 2, ctypes.byref(out)) == 2
+    assert L.kda_chunk_prefill_workspace(1, 64, 2, 128, 128, 64, 2, None) == 1
+
+
+def test_verify_commit_copy_host_errors(L):
+    P = pool()
+    # verify: q, k, v, g, b, in_dtype, o, n_req, L, H, dk, dv, pool, ckpt, u, kg, err, stream
+    v = lambda **kw: L.kda_recurrent_verify(*[kw.get(n, d) for n, d in [
+        ("q", FAKE), ("k", FAKE), ("v", FAKE), ("g", FAKE), ("b", FAKE), ("dt", 2), ("o", FAKE),
+        ("n", 4), ("L", 8), ("H", 2), ("dk", 128), ("dv", 128), ("pool", P), ("ck", FAKE),
+        ("u", FAKE), ("kg", FAKE), ("err", None), ("st", None)]])
+    assert v(L=0) == 1
+    assert v(L=257) == 2
+    assert v(dk=64, dv=64) == 2
+    assert v(o=None) == 1
+    assert v(n=-1) == 1
+    assert v(pool=pool(H=4)) == 1
+    assert v(n=0) == 0
+    c = lambda **kw: L.kda_commit(*[kw.get(n, d) for n, d in [
+        ("pool", P), ("ck", FAKE), ("dst", None), ("acc", FAKE), ("u", FAKE), ("kg", FAKE),
+        ("rdt", 2), ("n", 4), ("L", 8), ("H", 2), ("dk", 128), ("dv", 128), ("err", None),
+        ("st", None)]])
+    assert c(acc=None) == 1
+    assert c(rdt=5) == 2
+    assert c(L=300) == 2
+    assert c(n=0) == 0
+    s = lambda **kw: L.kda_state_copy(kw.get("pool", P), kw.get("src", FAKE), kw.get("dst", FAKE),
+                                      kw.get("n", 3), None, None)
+    assert s(n=-1) == 1
+    assert s(src=None) == 1
+    assert s(pool=pool(base=None)) == 1
+    assert s(pool=pool(dtype=1, H=1, dk=3, dv=1)) == 2   # 6-byte slots cannot be copied in 16-byte units
+    assert s(n=0) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(kda, "_lib", None)
+    monkeypatch.setattr(kda, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(kda.KdaError):
+        kda.lib()

@@ -1,0 +1,205 @@
+"""GPU parity of the state paths through the C ABI: kda_state_copy,
+kda_recurrent_verify and kda_commit against the fp64 oracle.
+
+Copy is bit-exact.  Verify and commit compute in fp32 from exactly the
+values the oracle receives; the bar is 1e-4 relative for fp32 inputs and
+2e-2 for bf16/fp16 inputs (per (request, head) Frobenius), with the
+records checked bitwise (kg_rec is a copy of the inputs).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_state_kda_amd as kda
+import workloads as wl
+from oracle import kda_oracle as ko
+from tests.gpu_util import DEV, TOL, i32, make_pool, rel, rel_per_head, to_math, untouched
+
+pytestmark = pytest.mark.gpu
+
+
+def fill_slots(pool, slots, pool_dtype, seed):
+    H, dv, dk = pool.shape[1:]
+    host = {}
+    for s in slots:
+        st = wl.pool_state(int(s), H, dk, dv, pool_dtype, seed)
+        pool[int(s)] = st.to(DEV)
+        host[int(s)] = st
+    return host
+
+
+# ---------------------------------------------------------------- copy
+
+@pytest.mark.parametrize("pool_dtype", ["f32", "bf16", "f16"])
+def test_copy_fork_matches_oracle_bitwise(pool_dtype):
+    case = wl.spec_case(n_req=256, L=8, H=32, d=128, pool_dtype=pool_dtype, seed=3)
+    n_slots = case["n_slots"]
+    pool = make_pool(n_slots, 32, 128, 128, pool_dtype)
+    srcs = sorted(set(case["fork_src"].tolist()))
+    host = fill_slots(pool, srcs, pool_dtype, 3)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kda.state_copy(pool, i32(case["fork_src"]), i32(case["fork_dst"]), dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    # oracle over the involved slots only (remapped to a compact host pool of raw bits)
+    itype = torch.int32 if pool_dtype == "f32" else torch.int16
+    involved = srcs + sorted(case["fork_dst"].tolist())
+    idx = {s: i for i, s in enumerate(involved)}
+    sentinel_bits = make_pool(1, 32, 128, 128, pool_dtype)[0].cpu().view(itype).numpy()
+    cpu_pool = np.stack([host[s].view(itype).numpy() if s in host else sentinel_bits for s in involved])
+    ref = ko.copy_ref(cpu_pool, [idx[s] for s in case["fork_src"].tolist()],
+                      [idx[d] for d in case["fork_dst"].tolist()])
+    got = pool[torch.as_tensor(involved, device=DEV)].cpu().view(itype).numpy()
+    assert np.array_equal(got, ref)
+    others = sorted(set(range(n_slots)) - set(involved))
+    assert untouched(pool, others, pool_dtype)
+
+
+def test_copy_edge_cases():
+    pool = make_pool(8, 2, 128, 128, "f32")
+    host = fill_slots(pool, [0, 1], "f32", 5)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    # src == dst is a no-op; an out-of-range pair is skipped and flagged
+    kda.state_copy(pool, i32([1, 0, 9]), i32([1, 3, 4]), dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() & kda.DEV_ERR_SLOT
+    assert torch.equal(pool[1].cpu(), host[1])
+    assert torch.equal(pool[3].cpu(), host[0])
+    assert untouched(pool, [2, 4, 5, 6, 7], "f32")
+    # zero pairs launches nothing
+    kda.state_copy(pool, i32([]), i32([]))
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- verify
+
+def run_verify_case(n_req, L, H, in_dtype, pool_dtype, seed):
+    d = 128
+    toks = wl.token_inputs(n_req * L, H, d, d, in_dtype, seed, shape_prefix=(n_req, L))
+    n_slots = n_req + 3
+    ckpt = wl.distinct_slots(n_req, n_slots, seed)
+    pool = make_pool(n_slots, H, d, d, pool_dtype)
+    host = fill_slots(pool, ckpt, pool_dtype, seed)
+    before = pool.clone()
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    dev = {n: toks[n].to(DEV) for n in "qkvgb"}
+    o, u_rec, kg_rec = kda.recurrent_verify(dev["q"], dev["k"], dev["v"], dev["g"], dev["b"], pool,
+                                            i32(ckpt), dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert torch.equal(pool, before)                      # checkpoints are read only
+    ex = {n: wl.exact(toks[n]) for n in "qkvgb"}
+    S0 = np.stack([np.swapaxes(wl.exact(host[int(s)]), -1, -2) for s in ckpt])
+    o_ref, u_ref, kg_ref, S_L = ko.verify_ref(ex["q"], ex["k"], ex["v"], ex["g"], ex["b"], S0)
+    return dict(o=wl.exact(o.cpu()), u=u_rec.cpu().double().numpy(), kg=kg_rec.cpu(),
+                o_ref=o_ref, u_ref=u_ref, kg_ref=kg_ref, toks=toks, ckpt=ckpt, pool=pool,
+                host=host, S0=S0, S_L=S_L, dev=dev, u_rec=u_rec, kg_rec=kg_rec, ex=ex)
+
+
+@pytest.mark.parametrize("in_dtype,pool_dtype", [("bf16", "f32"), ("f32", "f32"), ("bf16", "bf16"),
+                                                  ("f16", "f16"), ("f32", "bf16")])
+def test_verify_matches_oracle(in_dtype, pool_dtype):
+    r = run_verify_case(n_req=12, L=8, H=3, in_dtype=in_dtype, pool_dtype=pool_dtype, seed=21)
+    n_req = r["o"].shape[0]
+    tol = TOL[in_dtype]
+    for i in range(n_req):
+        assert rel_per_head(r["o"][i], r["o_ref"][i], 1) < tol
+        # u is computed in fp32 from exact inputs: hold it to the fp32 bar
+        assert rel_per_head(r["u"][i], r["u_ref"][i], 0) < 1e-4
+    # key / raw-gate records are lossless copies of the inputs
+    assert np.array_equal(wl.exact(r["kg"]), r["kg_ref"])
+
+
+def test_verify_full_spec_shape():
+    """256 requests x 32 heads x L = 8, bf16 inputs, fp32 pool (the
+    speculative-decode workload)."""
+    r = run_verify_case(n_req=256, L=8, H=32, in_dtype="bf16", pool_dtype="f32", seed=3)
+    worst_o = max(rel_per_head(r["o"][i], r["o_ref"][i], 1) for i in range(256))
+    assert worst_o < 2e-2
+    worst_u = max(rel_per_head(r["u"][i], r["u_ref"][i], 0) for i in range(256))
+    assert worst_u < 1e-4
+    assert np.array_equal(wl.exact(r["kg"]), r["kg_ref"])
+
+
+def test_verify_long_window():
+    """L = 256, the largest built window."""
+    r = run_verify_case(n_req=2, L=256, H=2, in_dtype="bf16", pool_dtype="f32", seed=22)
+    for i in range(2):
+        assert rel_per_head(r["o"][i], r["o_ref"][i], 1) < 2e-2
+        assert rel_per_head(r["u"][i], r["u_ref"][i], 0) < 1e-4
+
+
+# ---------------------------------------------------------------- commit
+
+@pytest.mark.parametrize("pool_dtype,in_dtype", [("f32", "bf16"), ("bf16", "bf16"), ("f16", "bf16"),
+                                                  ("f32", "f32")])
+def test_commit_matches_oracle(pool_dtype, in_dtype):
+    n_req, L, H, d = 24, 8, 2, 128
+    r = run_verify_case(n_req=n_req, L=L, H=H, in_dtype=in_dtype, pool_dtype=pool_dtype, seed=31)
+    acc = np.arange(n_req, dtype=np.int32) % (L + 1)     # every length 0..L, n = 0 included
+    pool = r["pool"]
+    ckpt = r["ckpt"]
+    before = pool.clone()
+    # oracle records = exactly the values handed to the kernel
+    u_in = r["u_rec"]
+    kg_in = r["kg_rec"]
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kda.commit(pool, i32(ckpt), i32(acc), u_in, kg_in, dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    u64 = u_in.cpu().double().numpy()
+    kg64 = wl.exact(kg_in.cpu())
+    tol = 1e-4 if pool_dtype == "f32" else 2e-2
+    for i in range(n_req):
+        s = int(ckpt[i])
+        got = to_math(pool[s])
+        ref = ko.commit_ref(r["S0"][i], kg64[i, :, :, :d], kg64[i, :, :, d:], u64[i], int(acc[i]))
+        if acc[i] == 0:
+            assert torch.equal(pool[s], before[s])       # in place, nothing accepted: untouched
+        else:
+            assert rel_per_head(got, ref, 0) < tol
+            # and the rebuilt state equals a replay of the accepted positions
+            rep = ko.replay_ref(*(r["ex"][n][i] for n in "qkvgb"), r["S0"][i], int(acc[i]))
+            assert rel_per_head(got, rep, 0) < max(tol, 2e-2 if in_dtype != "f32" else 1e-4)
+
+
+def test_commit_to_other_slot_and_errors():
+    n_req, L, H, d = 4, 8, 2, 128
+    r = run_verify_case(n_req=n_req, L=L, H=H, in_dtype="bf16", pool_dtype="f32", seed=41)
+    pool = r["pool"]
+    n_slots = pool.shape[0]
+    ckpt = r["ckpt"]
+    free = sorted(set(range(n_slots)) - set(ckpt.tolist()))
+    dst = np.array([free[0], free[1], ckpt[2], ckpt[3]], dtype=np.int32)
+    acc = np.array([0, 5, 3, 9], dtype=np.int32)          # request 3 asks for more than L
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    before = pool.clone()
+    kda.commit(pool, i32(ckpt), i32(acc), r["u_rec"], r["kg_rec"], dst_slot=i32(dst), dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() & kda.DEV_ERR_ACCEPT
+    assert torch.equal(pool[int(dst[0])], before[int(ckpt[0])])   # n = 0 to another slot = copy
+    assert torch.equal(pool[int(ckpt[3])], before[int(ckpt[3])])  # rejected request untouched
+    u64 = r["u_rec"].cpu().double().numpy()
+    kg64 = wl.exact(r["kg_rec"].cpu())
+    ref = ko.commit_ref(r["S0"][1], kg64[1, :, :, :d], kg64[1, :, :, d:], u64[1], 5)
+    assert rel_per_head(to_math(pool[int(dst[1])]), ref, 0) < 1e-4
+    assert torch.equal(pool[int(ckpt[1])], before[int(ckpt[1])])  # source kept
+
+
+def test_verify_commit_full_spec_shape():
+    """The full speculative-decode step: 256 requests, H = 32, L = 8,
+    accepted ~ U{0..8}, in-place commit, then fork 64 -> 4 x 64."""
+    case = wl.spec_case(seed=3)
+    r = run_verify_case(n_req=256, L=8, H=32, in_dtype="bf16", pool_dtype="f32", seed=3)
+    pool, ckpt = r["pool"], r["ckpt"]
+    acc = case["accepted"]
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kda.commit(pool, i32(ckpt), i32(acc), r["u_rec"], r["kg_rec"], dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    worst = 0.0
+    for i in range(0, 256, 8):                                      # sampled requests
+        rep = ko.replay_ref(*(r["ex"][n][i] for n in "qkvgb"), r["S0"][i], int(acc[i]))
+        worst = max(worst, rel_per_head(to_math(pool[int(ckpt[i])]), rep, 0))
+    assert worst < 1e-4
