@@ -87,7 +87,7 @@ def spec_setup(dev):
                 bytes=dict(verify=verify_bytes, commit=commit_bytes, copy=copy_bytes))
 
 
-def cpu_baseline(case, seconds_target=10.0):
+def cpu_baseline(case, seconds_target=20.0):
     """Time the fp64 oracle, single thread, on the first tokens of the prefill."""
     from threadpoolctl import threadpool_limits
     from oracle import kda_oracle as ko

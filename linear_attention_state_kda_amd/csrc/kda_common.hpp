@@ -166,6 +166,13 @@ template <> struct RegFrag<float, 16> {
   }
 };
 
+// Buffer resource (V#) for raw byte-addressed buffer loads and stores: base
+// address, byte range (accesses at offsets >= num_bytes read 0 / are dropped),
+// stride 0.  The third dword is the gfx9-family default data format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, 0x00020000);
+}
+
 __device__ __forceinline__ void set_err(int32_t* dev_err, uint32_t bits) {
   if (dev_err) atomicOr(reinterpret_cast<unsigned int*>(dev_err), bits);
 }
