@@ -115,6 +115,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-calibration", action="store_true",
+                    help="after the timed steps, run one kda_state_copy of 256 distinct fp32 "
+                         "slots (512 MiB read + 512 MiB written) so that FETCH_SIZE / WRITE_SIZE "
+                         "counters can be scaled against a copy of known size")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the KDA path here is built and timed on a single "
@@ -160,6 +164,11 @@ def main():
     ms = {c: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(a.steps)]))
           for i, c in enumerate(calls)}
     ms_step = wall / a.steps * 1e3
+    if a.traffic_calibration:
+        ck = sp["case"]["ckpt_slots"]
+        fresh = sorted(set(range(sp["case"]["n_slots"])) - set(ck.tolist()))[:len(ck)]
+        kda.state_copy(sp["pool"], i32(ck, dev), i32(fresh, dev))
+        torch.cuda.synchronize()
 
     p_s = ms["prefill"] * 1e-3
     tokens_per_s = T / p_s
