@@ -57,7 +57,9 @@
  *
  * Built shapes: (d_k, d_v, chunk) = (128, 128, 64) with bf16 or fp16 inputs,
  * and (16, 16, 16) with fp32 inputs.  Pools may be fp32, fp16 or bf16.  The
- * verify, commit and copy calls accept d_k = d_v in {16, 32, 64, 128}.
+ * verify and commit calls take d_k = d_v = 128 (other head sizes return
+ * KDA_ERR_UNSUPPORTED); the copy call takes any shape whose slot is a
+ * multiple of 16 bytes.
  */
 #ifndef KDA_H
 #define KDA_H

@@ -6,15 +6,21 @@
 // kernel, with the same fp32 code as the prefill path.
 //
 // One workgroup (4 waves) per (request, head); the d x d fp32 state stays in
-// registers.  Lane layout: a half-wave (32 lanes) spans one state row of 128
-// key entries, 4 consecutive entries per lane, so every load of the
-// checkpoint is a contiguous 1 KiB per wave; each lane holds 16 rows.  Per
-// token:
-//   pred_v = sum_k S[v][k] alpha_k k_k     -> u_v = beta (v_v - pred_v)
-//   oq_v   = sum_k S[v][k] alpha_k q_k     -> o_v = oq_v + u_v (k . q)
-//   S[v][k] = alpha_k S[v][k] + k_k u_v
-// (o = S_t^T q = (Diag(alpha) S)^T q + u (k . q)).  The two 32-lane dot
-// products per row are reduced through LDS.
+// registers.  An 8-lane group owns 4 state rows (v) and each lane 16 of their
+// 128 key entries, k in {4*(lane%8) + 32*j + e}, so each checkpoint load is
+// a contiguous 128 bytes per group.  Within a block of kTB positions the
+// state is held as S = Diag(D) St, D_t[k] being the product of alpha[k] over
+// the block's positions up to and including t.  Then, per position t:
+//   S_dec^T k = St^T (D_t k),  S_dec^T q = St^T (D_t q)     (S_dec = Diag(alpha_t) S)
+//   u = beta (v - S_dec^T k),  o = S_dec^T q + u (k . q)
+//   St += (k / D_t) u^T                                      (one FMA per element)
+// and at the end of a block St <- Diag(D) St restarts D at 1.  The two dot
+// products reduce across the 8 lanes of a group with DPP, so every lane gets
+// its own rows' u with no LDS traffic per position.  The per-position vectors
+// (D_t k, D_t q, k / D_t, v, beta, k . q) of a block are built once behind one
+// barrier.  D and 1/D stay finite in fp32 while the summed gate over a block
+// stays above about -80 (the chunked path's bound over a whole chunk is the
+// same, so verify is the less restrictive of the two).
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
@@ -23,9 +29,16 @@ namespace kda {
 namespace {
 
 constexpr int kT = 256;
-constexpr int kD = 128;          // state rows (d_v) and columns (d_k)
-constexpr int kRowsPerLane = 16; // 128 rows / (4 waves * 2 half-waves)
-constexpr int kRedLd = 33;       // padded row of the reduction scratch
+constexpr int kD = 128;   // state rows (d_v) and columns (d_k)
+constexpr int kTB = 8;    // positions prepared per block
+
+// Sum over the 8 lanes of a group, result in every lane of the group.
+__device__ __forceinline__ float group8_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));  // lane ^ 1
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));  // lane ^ 2
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, true)); // 7 - lane in 8
+  return x;
+}
 
 template <typename TIn, typename TPool>
 __global__ __launch_bounds__(kT) void kda_verify_kernel(
@@ -33,12 +46,17 @@ __global__ __launch_bounds__(kT) void kda_verify_kernel(
     const TIn* __restrict__ g, const TIn* __restrict__ bl, TIn* __restrict__ o, int n_req, int L,
     int H, const TPool* __restrict__ pool, int64_t n_slots, const int32_t* __restrict__ ckpt,
     float* __restrict__ u_rec, TIn* __restrict__ kg_rec, int32_t* __restrict__ dev_err) {
-  __shared__ float s_w[kD], s_x[kD], s_a[kD], s_k[kD], s_v[kD], s_u[kD];
-  __shared__ float s_kq[2], s_beta;
-  __shared__ float s_red[4][64 * kRedLd];
+  // per position of the block: D_t k, D_t q (for the dots), k / D_t (update), v
+  __shared__ __align__(16) float s_wk[kTB][kD];
+  __shared__ __align__(16) float s_wq[kTB][kD];
+  __shared__ __align__(16) float s_ku[kTB][kD];
+  __shared__ __align__(16) float s_v[kTB][kD];
+  __shared__ __align__(16) float s_dec[kD];      // D at the end of the block
+  __shared__ float s_beta[kTB], s_kq[2][kTB];    // k . q as two 64-channel halves
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int half = lane >> 5, kq = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = lane >> 3, gl = lane & 7;       // 8 groups of 8 lanes
   const int r = blockIdx.x / H, h = blockIdx.x % H;
   if (r >= n_req) return;
   const int slot = ckpt[r];
@@ -47,73 +65,116 @@ __global__ __launch_bounds__(kT) void kda_verify_kernel(
     return;
   }
 
-  // ---- checkpoint rows 32*wave + 2*i + half, key entries 4*kq..4*kq+3
-  floatx4 S[kRowsPerLane];
+  // ---- checkpoint: rows row0 + i (i < 4), keys 4*gl + 32*j + e
+  const int row0 = 32 * wave + 4 * grp;
+  floatx4 S[4][4];
   const TPool* src = pool + ((int64_t)slot * H + h) * kD * kD;
 #pragma unroll
-  for (int i = 0; i < kRowsPerLane; ++i) S[i] = load4(src + (32 * wave + 2 * i + half) * kD + 4 * kq);
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) S[i][j] = load4(src + (row0 + i) * kD + 4 * gl + 32 * j);
 
   const int64_t tok_stride = (int64_t)H * kD;
-  for (int t = 0; t < L; ++t) {
-    const int64_t base = ((int64_t)r * L + t) * tok_stride + (int64_t)h * kD;
-    // ---- per-token vectors
+  for (int t0 = 0; t0 < L; t0 += kTB) {
+    const int nb = min(kTB, L - t0);
+    if (t0 > 0) __syncthreads();  // every wave is done with the previous block
+    // ---- per-position vectors: threads 0..127 own one key channel each and
+    //      run the cumulative decay over the block; threads 128..255 load v
+    //      and beta.  Loads past the block end are clamped to its last
+    //      position (branch-free, so they all issue before the first use).
     if (tid < kD) {
-      const TIn kraw = k[base + tid], graw = g[base + tid];
-      const float kk = to_f32(kraw), qq = to_f32(q[base + tid]);
-      const float a = __expf(to_f32(graw));
-      s_w[tid] = a * kk;
-      s_x[tid] = a * qq;
-      s_a[tid] = a;
-      s_k[tid] = kk;
-      TIn* rec = kg_rec + (((int64_t)r * H + h) * L + t) * (2 * kD);
-      rec[tid] = kraw;
-      rec[kD + tid] = graw;
-      float p = kk * qq;
+      TIn kr[kTB], gr[kTB], qr[kTB];
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) p += __shfl_xor(p, m);
-      if (lane == 0) s_kq[wave] = p;
+      for (int jj = 0; jj < kTB; ++jj) {
+        const int64_t base = ((int64_t)r * L + t0 + min(jj, nb - 1)) * tok_stride + (int64_t)h * kD + tid;
+        kr[jj] = k[base];
+        gr[jj] = g[base];
+        qr[jj] = q[base];
+      }
+      float D = 1.f;
+#pragma unroll
+      for (int jj = 0; jj < kTB; ++jj) {
+        const float kk = to_f32(kr[jj]), qq = to_f32(qr[jj]);
+        D *= __expf(to_f32(gr[jj]));
+        s_wk[jj][tid] = D * kk;
+        s_wq[jj][tid] = D * qq;
+        s_ku[jj][tid] = kk / D;
+        float p = kk * qq;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) p += __shfl_xor(p, m);
+        if (lane == 0) s_kq[wave][jj] = p;
+        if (jj < nb) {
+          TIn* rec = kg_rec + (((int64_t)r * H + h) * L + t0 + jj) * (2 * kD);
+          rec[tid] = kr[jj];
+          rec[kD + tid] = gr[jj];
+        }
+      }
+      s_dec[tid] = D;  // read only when the block is full (a next block exists)
     } else {
-      s_v[tid - kD] = to_f32(v[base + tid - kD]);
-      if (tid == kD) s_beta = sigmoidf_(to_f32(bl[((int64_t)r * L + t) * H + h]));
+      const int c = tid - kD;
+      TIn vr[kTB];
+#pragma unroll
+      for (int jj = 0; jj < kTB; ++jj)
+        vr[jj] = v[((int64_t)r * L + t0 + min(jj, nb - 1)) * tok_stride + (int64_t)h * kD + c];
+      const TIn br = bl[((int64_t)r * L + t0 + min(c, nb - 1)) * H + h];
+#pragma unroll
+      for (int jj = 0; jj < kTB; ++jj) s_v[jj][c] = to_f32(vr[jj]);
+      if (c < kTB) s_beta[c] = sigmoidf_(to_f32(br));
     }
     __syncthreads();
 
-    const floatx4 w4 = *reinterpret_cast<const floatx4*>(&s_w[4 * kq]);
-    const floatx4 x4 = *reinterpret_cast<const floatx4*>(&s_x[4 * kq]);
-    float* red = s_red[wave];
+    for (int jj = 0; jj < nb; ++jj) {
+      const int t = t0 + jj;
+      floatx4 wk[4], wq[4];
 #pragma unroll
-    for (int i = 0; i < kRowsPerLane; ++i) {
-      const floatx4 s = S[i];
-      red[(half * 32 + i) * kRedLd + kq] = s[0] * w4[0] + s[1] * w4[1] + s[2] * w4[2] + s[3] * w4[3];
-      red[(half * 32 + 16 + i) * kRedLd + kq] = s[0] * x4[0] + s[1] * x4[1] + s[2] * x4[2] + s[3] * x4[3];
-    }
-    __syncthreads();
-    // lane j of the wave finishes output j: half_j = j / 32, quantity (j/16)&1, row i = j&15
-    float acc = 0.f;
-    {
-      const float* rr = red + lane * kRedLd;
+      for (int j = 0; j < 4; ++j) {
+        wk[j] = *reinterpret_cast<const floatx4*>(&s_wk[jj][4 * gl + 32 * j]);
+        wq[j] = *reinterpret_cast<const floatx4*>(&s_wq[jj][4 * gl + 32 * j]);
+      }
+      float pred[4], oq[4];
 #pragma unroll
-      for (int m = 0; m < 32; ++m) acc += rr[m];
-    }
-    const int hj = lane >> 5, qj = (lane >> 4) & 1, ij = lane & 15;
-    const int row = 32 * wave + 2 * ij + hj;
-    const float kqv = s_kq[0] + s_kq[1];
-    if (qj == 0) {
-      const float u = s_beta * (s_v[row] - acc);
-      s_u[row] = u;
-      u_rec[(((int64_t)r * H + h) * L + t) * kD + row] = u;
-    }
-    __syncthreads();
-    if (qj == 1) {
-      o[((int64_t)r * L + t) * tok_stride + (int64_t)h * kD + row] = from_f32<TIn>(acc + s_u[row] * kqv);
-    }
-    if (t + 1 < L) {
-      const floatx4 a4 = *reinterpret_cast<const floatx4*>(&s_a[4 * kq]);
-      const floatx4 k4 = *reinterpret_cast<const floatx4*>(&s_k[4 * kq]);
+      for (int i = 0; i < 4; ++i) {
+        float a = 0.f, b2 = 0.f;
 #pragma unroll
-      for (int i = 0; i < kRowsPerLane; ++i) S[i] = a4 * S[i] + k4 * s_u[32 * wave + 2 * i + half];
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a += S[i][j][e] * wk[j][e];
+            b2 += S[i][j][e] * wq[j][e];
+          }
+        pred[i] = group8_sum(a);
+        oq[i] = group8_sum(b2);
+      }
+      const float beta = s_beta[jj], kqv = s_kq[0][jj] + s_kq[1][jj];
+      float u[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) u[i] = beta * (s_v[jj][row0 + i] - pred[i]);
+      // lanes 0..3 of a group write u and lanes 4..7 write o, one row each
+      {
+        const int i = gl & 3;
+        const float ui = (i == 0) ? u[0] : (i == 1) ? u[1] : (i == 2) ? u[2] : u[3];
+        const float oqi = (i == 0) ? oq[0] : (i == 1) ? oq[1] : (i == 2) ? oq[2] : oq[3];
+        if (gl < 4) u_rec[(((int64_t)r * H + h) * L + t) * kD + row0 + i] = ui;
+        else o[((int64_t)r * L + t) * tok_stride + (int64_t)h * kD + row0 + i] = from_f32<TIn>(oqi + ui * kqv);
+      }
+      if (t + 1 < L) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const floatx4 ku = *reinterpret_cast<const floatx4*>(&s_ku[jj][4 * gl + 32 * j]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[i][j] += ku * u[i];
+        }
+      }
     }
-    __syncthreads();
+    // ---- rebase: St <- Diag(D_block) St, so the next block starts from D = 1
+    if (t0 + kTB < L) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const floatx4 d4 = *reinterpret_cast<const floatx4*>(&s_dec[4 * gl + 32 * j]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[i][j] = d4 * S[i][j];
+      }
+    }
   }
 }
 
