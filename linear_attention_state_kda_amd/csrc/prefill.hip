@@ -45,6 +45,8 @@ namespace kda {
 constexpr int kThreads = 256;
 constexpr int kXcd = 8;     // MI355X: workgroups are dealt round-robin to 8 XCDs
 constexpr int kFB = 1024;   // bytes of one fragment block: 64 lanes x 16 bytes
+constexpr int kNumCU = 256; // MI355X compute units
+constexpr int kSpreadLds = 72 * 1024;  // with the static part, > half of a CU's 160 KiB LDS
 
 // K-block sizes: 32 for the 16-bit 16x16x32 MFMAs; fp32 uses 16 so that one
 // lane's fragment is 16 bytes as well.
@@ -433,28 +435,6 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_prep(
 
 // ---------------------------------------------------------------- 3. scan
 
-template <int DK, int DV, int C, int BV, typename TOp>
-struct ScanSmem {
-  static constexpr int PADK = 16 / (int)sizeof(TOp);
-  static constexpr int LDK = DK + PADK;
-  static constexpr int LDT = C + PADK;
-  TOp s[BV * LDK];  // state tile as B operand, [v][pos(k)]
-  TOp y[BV * LDT];  // Diag(beta)(V - Kt S), [v][pos(t)]
-  TOp u[BV * LDT];  // U, [v][pos(t)]
-};
-
-// Per-wave operands of one chunk, loaded straight from the record.
-template <int DK, int C, int BV, typename TIn, typename TOp>
-struct ChunkOps {
-  static constexpr int KBK = KBOf<TOp>::v, KBT = KBOf<TOp>::v;
-  static constexpr int NK = DK / 16, NKW = (NK + 3) / 4, NVS = BV / 16;
-  static constexpr int NFK = DK / KBK, NFT = C / KBT, NFB = NKW * NFT;
-  uint4 kt[NFK], qt[NFK], t[NFT], p[NFT], kb[NFB];
-  floatx4 beta;
-  floatx4 dec[NKW];
-  typename std::conditional<sizeof(TIn) == 2, uint16_t, uint32_t>::type v[NVS][4];  // raw bits
-};
-
 template <typename T>
 __device__ __forceinline__ T bits_to(uint32_t b) {
   if constexpr (sizeof(T) == 2) {
@@ -491,29 +471,91 @@ __device__ __forceinline__ floatx4 ld16f(__amdgpu_buffer_rsrc_t r, int voff, int
   return f;
 }
 
-template <int DK, int DV, int C, int BV, typename TIn, typename TOp, typename TPool>
-__global__ __launch_bounds__(kThreads) void kda_chunk_scan(
+// K-blocks of T and P rows of token tile mt up to the diagonal, and the
+// index of block (mt, 0) among the lower (incl. diagonal) T blocks.
+template <int KB>
+__host__ __device__ constexpr int scan_nkb(int mt) { return (16 * mt + 15) / KB + 1; }
+template <int KB>
+__host__ __device__ constexpr int scan_tblk(int mt) {
+  int j = 0;
+  for (int m = 0; m < mt; ++m) j += scan_nkb<KB>(m);
+  return j;
+}
+
+// Scan geometry: four waves per (sequence, head, 16-column tile of S).
+// Wave w owns token tile w (rows of X, Y, O) and S K-block w (key tiles
+// w*KB/16 ...), so it loads only its own quarter of each record.
+template <int DK, int C, typename TOp>
+struct ScanGeom {
+  static constexpr int KB = KBOf<TOp>::v;
+  static constexpr int NT = C / 16, NK = DK / 16, NFK = DK / KB, NFT = C / KB;
+  static constexpr int KPW = KB / 16;  // key tiles per S K-block
+  __host__ __device__ static constexpr int nkb(int mt) { return scan_nkb<KB>(mt); }
+  __host__ __device__ static constexpr int tblk(int mt) { return scan_tblk<KB>(mt); }
+  static constexpr int NTB = scan_tblk<KB>(NT);
+  static_assert(NT <= 4 && NFK <= 4, "one token tile and one S K-block per wave");
+};
+
+template <int DK, int C, typename TIn, typename TOp>
+struct ScanRegs {
+  typedef ScanGeom<DK, C, TOp> G;
+  uint4 kt[G::NFK], qt[G::NFK], p[G::NFT], kb[G::KPW][G::NFT];
+  uint4 tb[(G::NTB + 3) / 4];    // the T blocks this wave copies into LDS
+  uint4 vv;                      // this wave's 1 KiB share of the chunk's V tile
+  uint4 bd;                      // wave 0: beta and e^Gamma_n (16 bytes per lane)
+};
+
+template <int DK, int C, typename TIn, typename TOp>
+struct ScanLds {
+  typedef ScanGeom<DK, C, TOp> G;
+  uint4 s[G::NFK][64];           // S as B fragments
+  uint4 y[G::NFT][64];           // Y = Diag(beta)(V - Kt S) as B fragments
+  uint4 t[G::NTB][64];           // lower T fragment blocks of the current chunk
+  float bd[2][C + DK];           // beta, e^Gamma_n; by chunk parity
+  TIn vb[C][16];                 // the chunk's V tile, row-major
+  TIn ob[C][16];                 // the chunk's output tile, row-major
+};
+
+// Four waves per (sequence, head, 16-column tile of S).  Per chunk:
+//   S fragments -> LDS, barrier;  X = Kt S and O = Qt S for the wave's token
+//   tile; Y and the chunk's T blocks -> LDS, barrier;  U = T Y for all token
+//   tiles (every wave, so U never has to be exchanged);  O += P U -> LDS;
+//   S = Diag(e^Gamma_n) S + Kb^T U for the wave's key tiles.
+// Accumulator tiles (lane l: column l%16, rows 4(l/16)+i) are B fragments of
+// the next product as they stand (fragment K-positions are permuted per
+// K-block, see pos_in_block), so S, Y and U go to LDS in fragment order and
+// come back with one 16-byte read per lane.  Each wave loads its share of
+// every record (its token tile's Kt, Qt, P rows, its key tiles' Kb^T rows,
+// a quarter of T) two chunks ahead, into registers.  Every global access
+// moves 16 bytes per lane: the address unit costs about the same per
+// instruction whatever the width, so the V tile, beta / e^Gamma_n and the
+// output tile go through LDS in 1 KiB pieces instead of per-lane scalars.
+template <int DK, int DV, int C, typename TIn, typename TOp, typename TPool>
+__global__ __launch_bounds__(256) void kda_chunk_scan(
     const TIn* __restrict__ v, TIn* __restrict__ o, const int32_t* __restrict__ cu, int n_seqs,
     int64_t total, int H, int64_t cap, const int32_t* __restrict__ off, const uint8_t* __restrict__ recs,
     TPool* __restrict__ pool, int64_t n_slots, const int32_t* __restrict__ init_slot,
     const int32_t* __restrict__ final_slot, const int32_t* __restrict__ track_ptr,
     const int32_t* __restrict__ track_chunk, const int32_t* __restrict__ track_slot, int n_track,
     float* __restrict__ track_f32, int32_t* __restrict__ dev_err) {
-  typedef ScanSmem<DK, DV, C, BV, TOp> Sm;
   typedef Rec<DK, C, TOp> R;
-  typedef ChunkOps<DK, C, BV, TIn, TOp> Ops;
-  constexpr int KBK = R::KBK, KBT = R::KBT;
-  constexpr int NT = C / 16, NK = DK / 16, NVS = BV / 16, NVT = DV / BV;
-  constexpr int NKW = Ops::NKW, NFK = Ops::NFK, NFT = Ops::NFT;
-  extern __shared__ __align__(16) uint8_t smem_raw[];
-  Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
-  typedef typename Frag<TOp, KBK>::type FKt;
-  typedef typename Frag<TOp, KBT>::type FTt;
-  typedef Frag<TOp, KBK> FK;
-  typedef Frag<TOp, KBT> FT;
+  typedef ScanGeom<DK, C, TOp> G;
+  typedef ScanRegs<DK, C, TIn, TOp> Regs;
+  constexpr int KB = G::KB, NFK = G::NFK, NFT = G::NFT, KPW = G::KPW, NTB = G::NTB;
+  constexpr int BV = 16, NVT = DV / BV;
+  // V / o tile: 16-byte pieces, LPR per row, RPI rows per 1 KiB instruction
+  constexpr int LPR = BV * (int)sizeof(TIn) / 16, RPI = 64 / LPR, NVQ = C / RPI;
+  constexpr int NBD = (C + DK) * 4 / 16;  // lanes holding beta / e^Gamma_n
+  static_assert(NVQ >= 1 && NVQ <= 4 && C % RPI == 0 && NBD <= 64, "scan tile shapes");
+  static_assert(R::kDec == R::kBeta + C * 4, "beta and e^Gamma_n are contiguous");
+  typedef typename Frag<TOp, KB>::type FT;
+  typedef RegFrag<TOp, KB> RF;
+  __shared__ ScanLds<DK, C, TIn, TOp> sm;
 
   const int tid = threadIdx.x, lane = tid & 63, g16 = lane >> 4, l16 = lane & 15;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
+  const bool has_tile = w < G::NT, has_keys = w < NFK, has_vq = w < NVQ;
+  const int mt = has_tile ? w : 0, kf = has_keys ? w : 0;
   // XCD-aware decode: all NVT tiles of one (seq, head) pair share blockIdx % 8.
   const int xcd = blockIdx.x % kXcd, slot_ = blockIdx.x / kXcd;
   const int vt = slot_ % NVT;
@@ -524,11 +566,6 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_scan(
   if (!seq_ok(cu, off, seq, total, C, t_beg, len, nch)) return;
   const int v0 = vt * BV;
   const bool lead = (vt == 0 && h == 0);
-  const int m = wave;  // token tile of this wave
-  // With 4 waves: every wave owns a token tile when C >= 64 and two state
-  // tiles when d_k = 128; the guards below fold away in that case.
-  constexpr bool kAllTiles = NT >= 4;
-  constexpr bool kAllK = NK >= 4 * NKW;
 
   // ---- tracks of this sequence (CSR)
   int e0 = 0, e1 = 0;
@@ -541,220 +578,226 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_scan(
     }
   }
   if (lead) {
-    for (int e = e0 + tid; e < e1; e += kThreads) {
+    for (int e = e0 + tid; e < e1; e += 256) {
       const int ce = track_chunk[e], se = track_slot[e];
       if (ce < 0 || ce > len / C) set_err(dev_err, 1u << 1);
       if (se < -1 || (int64_t)se >= n_slots) set_err(dev_err, 1u);
     }
   }
 
-  // ---- initial state: S[k][v] = pool[init][h][v][k]
-  floatx4 S[NKW][NVS];
+  // ---- initial state, the wave's key tiles: S[k][v] = pool[init][h][v][k]
+  floatx4 S[KPW];
+  const int64_t st_off = (int64_t)(v0 + l16) * DK + 16 * KPW * kf + 4 * g16;  // lane's first element
   {
     const int is = init_slot[seq];
-    const bool ok = is >= 0 && (int64_t)is < n_slots;
-    if (!ok && is != -1 && lead && tid == 0) set_err(dev_err, 1u);
+    const bool ok = is >= 0 && (int64_t)is < n_slots && has_keys;
+    if (is != -1 && !(is >= 0 && (int64_t)is < n_slots) && lead && tid == 0) set_err(dev_err, 1u);
+    const TPool* src = pool + ((int64_t)(ok ? is : 0) * H + h) * DV * DK + st_off;
 #pragma unroll
-    for (int a = 0; a < NKW; ++a)
+    for (int j = 0; j < KPW; ++j) {
+      S[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (ok) S[j] = load4(src + 16 * j);
+    }
+    // Complete these loads here, so that the waits inside the chunk loop
+    // stay partial (the loop head cannot tell the first iteration apart).
 #pragma unroll
-      for (int vs = 0; vs < NVS; ++vs) {
-        S[a][vs] = floatx4{0.f, 0.f, 0.f, 0.f};
-        const int kt = wave + 4 * a;
-        if (ok && kt < NK) {
-          const int vv = v0 + 16 * vs + l16, kk = 16 * kt + 4 * g16;
-          S[a][vs] = load4(pool + (((int64_t)is * H + h) * DV + vv) * DK + kk);
-        }
-      }
+    for (int j = 0; j < KPW; ++j) asm volatile("" : "+v"(S[j]));
   }
 
+  // Snapshots: `next_snap` is the smallest requested chunk index >= the
+  // current one, so the per-chunk test is one scalar compare and the track
+  // list is read only when a snapshot is due.
+  auto next_track = [&](int c) {
+    int best = INT32_MAX;
+    for (int e = e0; e < e1; ++e) {
+      const int ce = track_chunk[e];
+      if (ce >= c && ce < best) best = ce;
+    }
+    return best;
+  };
+  int next_snap = next_track(0);
   auto snapshot = [&](int c) {
+    if (c != next_snap) return;
     for (int e = e0; e < e1; ++e) {
       if (track_chunk[e] != c) continue;
       const int se = track_slot[e];
       const bool to_pool = se >= 0 && (int64_t)se < n_slots;
+      if (has_keys) {
 #pragma unroll
-      for (int a = 0; a < NKW; ++a)
-#pragma unroll
-        for (int vs = 0; vs < NVS; ++vs) {
-          const int kt = wave + 4 * a;
-          if (kt >= NK) continue;
-          const int vv = v0 + 16 * vs + l16, kk = 16 * kt + 4 * g16;
-          if (track_f32) store4(track_f32 + (((int64_t)e * H + h) * DV + vv) * DK + kk, S[a][vs]);
-          if (to_pool) store4(pool + (((int64_t)se * H + h) * DV + vv) * DK + kk, S[a][vs]);
+        for (int j = 0; j < KPW; ++j) {
+          if (track_f32) store4(track_f32 + ((int64_t)e * H + h) * DV * DK + st_off + 16 * j, S[j]);
+          if (to_pool) store4(pool + ((int64_t)se * H + h) * DV * DK + st_off + 16 * j, S[j]);
         }
+      }
     }
+    next_snap = next_track(c + 1);
   };
 
   const int64_t vrow = (int64_t)H * DV;
-  const int nkb_m = (16 * m + 15) / KBT + 1;  // K-blocks of T and P rows up to the diagonal
-
-  // ---- issue the loads of chunk c's operands.  Buffer loads: the base is a
-  //      per-chunk resource in scalar registers and every per-lane offset is a
-  //      constant, so the loads cost almost no vector ALU work, and there are
-  //      no branches, so they stay in flight while the previous chunk is
-  //      computed.  V reads past the chunk's last row return 0 (range check);
-  //      those rows have beta = 0 and zero keys in any case.
-  const int mt = m < NT ? m : NT - 1;
   const int lane_off = lane * 16;
-  const int beta_off = (16 * mt + 4 * g16) * 4;
-  int dec_off[NKW];
-#pragma unroll
-  for (int a = 0; a < NKW; ++a) dec_off[a] = (16 * min(wave + 4 * a, NK - 1) + 4 * g16) * 4;
-  int v_off[NVS][4];  // byte offsets of this lane's V / o elements inside a chunk
-#pragma unroll
-  for (int vs = 0; vs < NVS; ++vs)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      v_off[vs][i] = (int)(((int64_t)(16 * mt + 4 * g16 + i) * vrow + 16 * vs + l16) * (int)sizeof(TIn));
+  // V / o piece of this lane in wave w's 1 KiB instruction: row, 16-byte part
+  const int vq_row = RPI * w + lane / LPR, vq_part = lane % LPR;
+  const int vq_off = (int)((int64_t)vq_row * vrow * (int)sizeof(TIn)) + 16 * vq_part;
   const uint8_t* rec_seq = recs + ((int64_t)h * cap + off[seq]) * R::kBytes;
 
+  // Per-chunk buffer resources: the record, and the chunk's rows of V / o
+  // (reads past the last row return 0 and stores there are dropped; those
+  // rows carry beta = 0 and zero keys in the record as well).
+  auto rec_rsrc = [&](int c) { return buffer_rsrc(rec_seq + (int64_t)c * R::kBytes, R::kBytes); };
   auto rows_rsrc = [&](const TIn* base, int c) {
     const int n = min(C, len - c * C);
     const TIn* p = base + (int64_t)(t_beg + c * C) * vrow + (int64_t)h * DV + v0;
     return buffer_rsrc(p, (uint32_t)(((int64_t)(n - 1) * vrow + BV) * (int)sizeof(TIn)));
   };
-
-  auto load_ops = [&](Ops& op, int c) {
-    const auto rs = buffer_rsrc(rec_seq + (int64_t)c * R::kBytes, R::kBytes);
+  // Record offsets of the T blocks this wave copies: lower block j = w + 4 jj
+  // (clamped to the last one; only j < NTB is written to LDS).
+  int t_src[(NTB + 3) / 4];
+#pragma unroll
+  for (int jj = 0; jj < (NTB + 3) / 4; ++jj) {
+    const int j = min(w + 4 * jj, NTB - 1);
+    int m = 0;
+    while (m + 1 < G::NT && G::tblk(m + 1) <= j) ++m;
+    t_src[jj] = (m * NFT + (j - G::tblk(m))) * kFB;
+  }
+  // Operand groups, each issued once the current chunk is done with its registers.
+  auto ld_front = [&](Regs& r, int c) {  // Kt, Qt rows of the token tile; T, V, beta shares
+    const auto rs = rec_rsrc(c);
 #pragma unroll
     for (int f = 0; f < NFK; ++f) {
-      op.kt[f] = ld16(rs, lane_off, R::kKt + (mt * NFK + f) * kFB);
-      op.qt[f] = ld16(rs, lane_off, R::kQt + (mt * NFK + f) * kFB);
+      r.kt[f] = ld16(rs, lane_off, R::kKt + (mt * NFK + f) * kFB);
+      r.qt[f] = ld16(rs, lane_off, R::kQt + (mt * NFK + f) * kFB);
     }
 #pragma unroll
-    for (int f = 0; f < NFT; ++f) {
-      op.t[f] = ld16(rs, lane_off, R::kT + (mt * NFT + f) * kFB);
-      op.p[f] = ld16(rs, lane_off, R::kP + (mt * NFT + f) * kFB);
+    for (int jj = 0; jj < (NTB + 3) / 4; ++jj) r.tb[jj] = ld16(rs, lane_off, R::kT + t_src[jj]);
+    if (has_vq) r.vv = ld16(rows_rsrc(v, c), vq_off, 0);
+    if (w == 0) r.bd = ld16(rs, lane_off, R::kBeta);  // lanes past the record end read 0
+  };
+  auto ld_p = [&](Regs& r, int c) {
+    const auto rs = rec_rsrc(c);
+#pragma unroll
+    for (int f = 0; f < NFT; ++f)
+      if (f < G::nkb(mt)) r.p[f] = ld16(rs, lane_off, R::kP + (mt * NFT + f) * kFB);
+  };
+  auto ld_back = [&](Regs& r, int c) {  // Kb^T rows of the wave's key tiles
+    const auto rs = rec_rsrc(c);
+#pragma unroll
+    for (int j = 0; j < KPW; ++j) {
+      const int kt = KPW * kf + j;
+#pragma unroll
+      for (int f = 0; f < NFT; ++f) r.kb[j][f] = ld16(rs, lane_off, R::kKbT + (kt * NFT + f) * kFB);
     }
-    op.beta = ld16f(rs, beta_off, R::kBeta);
-#pragma unroll
-    for (int a = 0; a < NKW; ++a) {
-      const int kt = min(wave + 4 * a, NK - 1);
-#pragma unroll
-      for (int f = 0; f < NFT; ++f) op.kb[a * NFT + f] = ld16(rs, lane_off, R::kKbT + (kt * NFT + f) * kFB);
-      op.dec[a] = ld16f(rs, dec_off[a], R::kDec);
-    }
-    const auto rv = rows_rsrc(v, c);
-#pragma unroll
-    for (int vs = 0; vs < NVS; ++vs)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (sizeof(TIn) == 2) op.v[vs][i] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rv, v_off[vs][i], 0, 0);
-        else op.v[vs][i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rv, v_off[vs][i], 0, 0);
-      }
+  };
+  // Output tile of chunk c (in LDS since the previous barrier) -> o.
+  auto store_o = [&](int c) {
+    if (has_vq)
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int,
+                             *reinterpret_cast<const uint4*>(&sm.ob[vq_row][vq_part * (16 / sizeof(TIn))])),
+          rows_rsrc(o, c), vq_off, 0, 0);
   };
 
-  // ---- the state-dependent part of one chunk
-  auto step = [&](const Ops& op, int c) {
-    // state tile -> LDS as the B operand of Kt S and Qt S
-#pragma unroll
-    for (int a = 0; a < NKW; ++a) {
-      const int kt = wave + 4 * a;
-      if (!kAllK && kt >= NK) continue;
-#pragma unroll
-      for (int vs = 0; vs < NVS; ++vs)
-        store4(&sm.s[(16 * vs + l16) * Sm::LDK + pos_of<KBK>(16 * kt + 4 * g16)], S[a][vs]);
-    }
+  // ---- one chunk.  `r` holds chunk c's operands; chunk c + 2's are loaded
+  //      into it as its groups fall free (unconditional, clamped: the
+  //      waits stay partial).  bp = c % 2.
+  auto step = [&](Regs& r, int c, int bp) {
+    const int c2 = min(c + 2, nch - 1);
+    snapshot(c);
+    if (has_keys) sm.s[kf][lane] = __builtin_bit_cast(uint4, RF::make(S[0], S[KPW - 1]));
+    if (has_vq) *reinterpret_cast<uint4*>(&sm.vb[vq_row][vq_part * (16 / sizeof(TIn))]) = r.vv;
+    if (w == 0 && lane < NBD) *reinterpret_cast<uint4*>(&sm.bd[bp][4 * lane]) = r.bd;
     __syncthreads();
-    // X = Kt S, O = Qt S, Y = Diag(beta)(V - X)
-    floatx4 O[NVS];
-    if (kAllTiles || m < NT) {
+    if (c > 0) store_o(c - 1);
+    // X = Kt S, O = Qt S for the token tile;  Y = Diag(beta)(V - X)
+    floatx4 X = {0.f, 0.f, 0.f, 0.f}, O = X;
+    if (has_tile) {
 #pragma unroll
-      for (int vs = 0; vs < NVS; ++vs) {
-        floatx4 X = {0.f, 0.f, 0.f, 0.f};
-        O[vs] = X;
-        const TOp* srow = sm.s + (16 * vs + l16) * Sm::LDK;
+      for (int f = 0; f < NFK; ++f) {
+        const FT sf = __builtin_bit_cast(FT, sm.s[f][lane]);
+        X = mma(X, as_frag<FT>(r.kt[f]), sf);
+        O = mma(O, as_frag<FT>(r.qt[f]), sf);
+      }
+      const floatx4 beta = *reinterpret_cast<const floatx4*>(&sm.bd[bp][16 * mt + 4 * g16]);
+      floatx4 Y;
 #pragma unroll
-        for (int kb = 0; kb < NFK; ++kb) {
-          const FKt sf = FK::load(srow, kb, g16);
-          X = mma(X, as_frag<FKt>(op.kt[kb]), sf);
-          O[vs] = mma(O[vs], as_frag<FKt>(op.qt[kb]), sf);
-        }
-        floatx4 Y;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Y[i] = op.beta[i] * (to_f32(bits_to<TIn>(op.v[vs][i])) - X[i]);
-        store4(&sm.y[(16 * vs + l16) * Sm::LDT + pos_of<KBT>(16 * m + 4 * g16)], Y);
+      for (int i = 0; i < 4; ++i) Y[i] = beta[i] * (to_f32(sm.vb[16 * mt + 4 * g16 + i][l16]) - X[i]);
+      // token tile mt is half (mt % KPW) of Y K-block mt / KPW
+      if constexpr (KB == 32) {
+        const auto yf = RF::make(Y, Y);  // low half holds this tile's four values
+        uint2 lo4;
+        __builtin_memcpy(&lo4, &yf, 8);
+        reinterpret_cast<uint2*>(&sm.y[mt / KPW][lane])[mt % KPW] = lo4;
+      } else {
+        sm.y[mt][lane] = __builtin_bit_cast(uint4, RF::make(Y, Y));
       }
     }
+#pragma unroll
+    for (int jj = 0; jj < (NTB + 3) / 4; ++jj)
+      if (w + 4 * jj < NTB) sm.t[w + 4 * jj][lane] = r.tb[jj];
     __syncthreads();
-    // U = T Y  (T lower triangular: only K-blocks up to the diagonal)
-    if (kAllTiles || m < NT) {
+    ld_front(r, c2);
+    // U = T Y for every token tile (T lower triangular: K-blocks up to the diagonal)
+    FT yf[NFT];
 #pragma unroll
-      for (int vs = 0; vs < NVS; ++vs) {
-        floatx4 U = {0.f, 0.f, 0.f, 0.f};
-        const TOp* yrow = sm.y + (16 * vs + l16) * Sm::LDT;
+    for (int f = 0; f < NFT; ++f) yf[f] = __builtin_bit_cast(FT, sm.y[f][lane]);
+    floatx4 U[G::NT];
 #pragma unroll
-        for (int kb = 0; kb < NFT; ++kb)
-          if (kb < nkb_m) U = mma(U, as_frag<FTt>(op.t[kb]), FT::load(yrow, kb, g16));
-        store4(&sm.u[(16 * vs + l16) * Sm::LDT + pos_of<KBT>(16 * m + 4 * g16)], U);
-      }
+    for (int m = 0; m < G::NT; ++m) {
+      U[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int f = 0; f < NFT; ++f)
+        if (f < G::nkb(m)) U[m] = mma(U[m], __builtin_bit_cast(FT, sm.t[G::tblk(m) + f][lane]), yf[f]);
     }
-    __syncthreads();
-    // O += P U -> o;  S = Diag(e^Gamma_n) S + Kb^T U
-    const auto ro = rows_rsrc(o, c);
+    FT uf[NFT];
 #pragma unroll
-    for (int vs = 0; vs < NVS; ++vs) {
-      const TOp* urow = sm.u + (16 * vs + l16) * Sm::LDT;
-      FTt uf[NFT];
+    for (int f = 0; f < NFT; ++f) uf[f] = (KB == 32) ? RF::make(U[2 * f], U[(2 * f + 1) % G::NT]) : RF::make(U[f], U[f]);
+    // O += P U -> output tile in LDS (stored after the next barrier)
+    if (has_tile) {
 #pragma unroll
-      for (int kb = 0; kb < NFT; ++kb) uf[kb] = FT::load(urow, kb, g16);
-      if (kAllTiles || m < NT) {
+      for (int f = 0; f < NFT; ++f)
+        if (f < G::nkb(mt)) O = mma(O, as_frag<FT>(r.p[f]), uf[f]);
 #pragma unroll
-        for (int kb = 0; kb < NFT; ++kb)
-          if (kb < nkb_m) O[vs] = mma(O[vs], as_frag<FTt>(op.p[kb]), uf[kb]);
-        // rows past the chunk's end fall outside the resource and are dropped
+      for (int i = 0; i < 4; ++i) sm.ob[16 * mt + 4 * g16 + i][l16] = from_f32<TIn>(O[i]);
+    }
+    ld_p(r, c2);
+    // S = Diag(e^Gamma_n) S + Kb^T U for the wave's key tiles
+    if (has_keys) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t bits = to_bits(from_f32<TIn>(O[vs][i]));
-          if constexpr (sizeof(TIn) == 2) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)bits, ro, v_off[vs][i], 0, 0);
-          else __builtin_amdgcn_raw_buffer_store_b32(bits, ro, v_off[vs][i], 0, 0);
-        }
-      }
-#pragma unroll
-      for (int a = 0; a < NKW; ++a) {
-        const int kt = wave + 4 * a;
-        if (!kAllK && kt >= NK) continue;
+      for (int j = 0; j < KPW; ++j) {
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < NFT; ++kb) acc = mma(acc, as_frag<FTt>(op.kb[a * NFT + kb]), uf[kb]);
-        S[a][vs] = op.dec[a] * S[a][vs] + acc;
+        for (int f = 0; f < NFT; ++f) acc = mma(acc, as_frag<FT>(r.kb[j][f]), uf[f]);
+        const floatx4 dec = *reinterpret_cast<const floatx4*>(&sm.bd[bp][C + 16 * (KPW * kf + j) + 4 * g16]);
+        S[j] = dec * S[j] + acc;
       }
     }
-    // No trailing barrier: the next chunk's LDS writes come after barriers
-    // that a wave passes only once every wave has finished this chunk's reads.
+    ld_back(r, c2);
   };
 
-  Ops opA, opB;
-  if (nch > 0) load_ops(opA, 0);
+  Regs rA, rB;
+  if (nch > 0) {
+    ld_front(rA, 0); ld_p(rA, 0); ld_back(rA, 0);
+    const int c1 = min(1, nch - 1);
+    ld_front(rB, c1); ld_p(rB, c1); ld_back(rB, c1);
+  }
   int c = 0;
   for (; c + 1 < nch; c += 2) {
-    snapshot(c);
-    load_ops(opB, c + 1);
-    step(opA, c);
-    snapshot(c + 1);
-    // unconditional (a redundant reload of the last chunk at the end) so that
-    // the waits for opB above stay partial
-    load_ops(opA, min(c + 2, nch - 1));
-    step(opB, c + 1);
+    step(rA, c, 0);
+    step(rB, c + 1, 1);
   }
-  if (c < nch) {
-    snapshot(c);
-    step(opA, c);
+  if (c < nch) step(rA, c, 0);
+  if (nch > 0) {
+    __syncthreads();
+    store_o(nch - 1);
   }
   if (len % C == 0) snapshot(nch);
 
   // ---- final state, one cast into the pool dtype
   const int fs = final_slot[seq];
   if (fs >= 0 && (int64_t)fs < n_slots) {
+    if (has_keys) {
 #pragma unroll
-    for (int a = 0; a < NKW; ++a)
-#pragma unroll
-      for (int vs = 0; vs < NVS; ++vs) {
-        const int kt = wave + 4 * a;
-        if (kt >= NK) continue;
-        const int vv = v0 + 16 * vs + l16, kk = 16 * kt + 4 * g16;
-        store4(pool + (((int64_t)fs * H + h) * DV + vv) * DK + kk, S[a][vs]);
-      }
+      for (int j = 0; j < KPW; ++j) store4(pool + ((int64_t)fs * H + h) * DV * DK + st_off + 16 * j, S[j]);
+    }
   } else if (fs != -1 && lead && tid == 0) {
     set_err(dev_err, 1u);
   }
@@ -762,12 +805,13 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_scan(
 
 // ---------------------------------------------------------------- host side
 
+
+
 namespace {
 
-template <int DK, int DV, int C, int BV, typename TIn, typename TOp, typename TPool>
+template <int DK, int DV, int C, typename TIn, typename TOp, typename TPool>
 hipError_t run(const PrefillArgs& a, hipStream_t st) {
   typedef PrepSmem<DK, C, TOp> SmP;
-  typedef ScanSmem<DK, DV, C, BV, TOp> SmS;
   const int64_t cap = chunk_upper_bound(a.total_tokens, a.n_seqs, C);
   uint8_t* ws = static_cast<uint8_t*>(a.workspace);
   int32_t* off = reinterpret_cast<int32_t*>(ws);
@@ -785,11 +829,19 @@ hipError_t run(const PrefillArgs& a, hipStream_t st) {
                        static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.b), a.cu_seqlens,
                        a.n_seqs, a.total_tokens, a.H, cap, off, recs);
   }
-  auto ks = kda_chunk_scan<DK, DV, C, BV, TIn, TOp, TPool>;
-  const int sms = (int)sizeof(SmS);
+  auto ks = kda_chunk_scan<DK, DV, C, TIn, TOp, TPool>;
   const int64_t pairs = (int64_t)a.n_seqs * a.H;
-  const int64_t blocks = (pairs + kXcd - 1) / kXcd * kXcd * (DV / BV);
-  hipLaunchKernelGGL(ks, dim3((unsigned)blocks), dim3(kThreads), sms, st,
+  const int64_t blocks = (pairs + kXcd - 1) / kXcd * kXcd * (DV / 16);
+  // Each scan wave streams its whole record through its CU's vector memory
+  // path, which one wave nearly saturates.  When there are no more waves
+  // than CUs, reserve enough LDS (unused) that no two of them share a CU.
+  int lds_pad = 0;
+  if (blocks <= kNumCU) {
+    lds_pad = kSpreadLds;
+    hipError_t e = hipFuncSetAttribute((const void*)ks, hipFuncAttributeMaxDynamicSharedMemorySize, lds_pad);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(ks, dim3((unsigned)blocks), dim3(256), lds_pad, st,
                      static_cast<const TIn*>(a.v), static_cast<TIn*>(a.o), a.cu_seqlens, a.n_seqs,
                      a.total_tokens, a.H, cap, off, recs, static_cast<TPool*>(a.pool.base),
                      a.pool.n_slots, a.init_slot, a.final_slot, a.track_ptr, a.track_chunk,
@@ -797,12 +849,12 @@ hipError_t run(const PrefillArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int DK, int DV, int C, int BV, typename TIn, typename TOp>
+template <int DK, int DV, int C, typename TIn, typename TOp>
 hipError_t by_pool(const PrefillArgs& a, hipStream_t st) {
   switch (a.pool.dtype) {
-    case F32: return run<DK, DV, C, BV, TIn, TOp, float>(a, st);
-    case F16: return run<DK, DV, C, BV, TIn, TOp, f16>(a, st);
-    case BF16: return run<DK, DV, C, BV, TIn, TOp, bf16>(a, st);
+    case F32: return run<DK, DV, C, TIn, TOp, float>(a, st);
+    case F16: return run<DK, DV, C, TIn, TOp, f16>(a, st);
+    case BF16: return run<DK, DV, C, TIn, TOp, bf16>(a, st);
   }
   return hipErrorInvalidValue;
 }
@@ -828,11 +880,11 @@ size_t prefill_workspace_bytes(int n_seqs, int64_t total_tokens, int H, int dk, 
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   if (a.dk == 128 && a.dv == 128 && a.chunk == 64) {
-    if (a.in_dtype == BF16) return by_pool<128, 128, 64, 16, bf16, bf16>(a, st);
-    if (a.in_dtype == F16) return by_pool<128, 128, 64, 16, f16, f16>(a, st);
+    if (a.in_dtype == BF16) return by_pool<128, 128, 64, bf16, bf16>(a, st);
+    if (a.in_dtype == F16) return by_pool<128, 128, 64, f16, f16>(a, st);
   }
   if (a.dk == 16 && a.dv == 16 && a.chunk == 16 && a.in_dtype == F32)
-    return by_pool<16, 16, 16, 16, float, float>(a, st);
+    return by_pool<16, 16, 16, float, float>(a, st);
   return hipErrorInvalidValue;
 }
 
