@@ -33,6 +33,8 @@ import linear_attention_state_kda_amd as kda  # noqa: E402
 import workloads as wl  # noqa: E402
 
 HBM_PEAK = 8.0e12            # bytes/s, MI355X HBM3E
+CSRC = os.path.join(ROOT, "linear_attention_state_kda_amd", "csrc")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "prefill_traffic.md")
 BF16_PEAK = 2.5e15           # FLOP/s, dense bf16 MFMA
 METRIC = "KDA chunk-prefill tokens/s + %MFMA peak; verify/commit state GB/s + %HBM"
 
@@ -85,6 +87,25 @@ def spec_setup(dev):
                 ckpt=i32(case["ckpt_slots"], dev), acc=i32(acc, dev),
                 src=i32(case["fork_src"], dev), dst=i32(case["fork_dst"], dev),
                 bytes=dict(verify=verify_bytes, commit=commit_bytes, copy=copy_bytes))
+
+
+def measured_prefill_traffic():
+    """HBM bytes per prefill call from the committed FETCH_SIZE / WRITE_SIZE
+    profile (already scaled by the copy calibration), or None when the
+    prefill sources changed since those counters were taken."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("prefill.hip", "kda_common.hpp", "kda_launch.hpp"):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    try:
+        fields = dict(line.split(": ", 1) for line in open(TRAFFIC_PROFILE).read().splitlines()
+                      if line.startswith(("traffic_bytes_per_call: ", "source_sha256_16: ")))
+    except OSError:
+        return None
+    if fields.get("source_sha256_16", "").strip() != h.hexdigest()[:16]:
+        return None
+    return int(fields["traffic_bytes_per_call"])
 
 
 def cpu_baseline(case, seconds_target=20.0):
@@ -178,7 +199,7 @@ def main():
         achieved = p_bytes / p_s / 1e9
         roof = {"kernel": "kda_chunk_prefill (kda_chunk_map + kda_chunk_prep + kda_chunk_scan)",
                 "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                "frac": achieved * 1e9 / HBM_PEAK, "traffic": None,
+                "frac": achieved * 1e9 / HBM_PEAK, "traffic": measured_prefill_traffic(),
                 "algorithmic_bytes_per_launch": p_bytes, "avg_launch_ms": ms["prefill"]}
     else:
         achieved = gbs[dominant]
