@@ -104,6 +104,9 @@ kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, con
   if (q == nullptr || k == nullptr || v == nullptr || g == nullptr || b == nullptr ||
       o == nullptr || ckpt_slot == nullptr || u_rec == nullptr || kg_rec == nullptr)
     return KDA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16) || !aligned(o, 16) ||
+      !aligned(u_rec, 16) || !aligned(kg_rec, 16))
+    return KDA_ERR_INVALID_ARG;
   if ((int64_t)n_req * H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
   kda::VerifyArgs a{q, k, v, g, b, o, in_dtype, n_req, L, H, d_k, pool_desc(pool), ckpt_slot,
                     u_rec, kg_rec, dev_err};

@@ -46,13 +46,20 @@ __global__ __launch_bounds__(kT) void kda_verify_kernel(
     const TIn* __restrict__ g, const TIn* __restrict__ bl, TIn* __restrict__ o, int n_req, int L,
     int H, const TPool* __restrict__ pool, int64_t n_slots, const int32_t* __restrict__ ckpt,
     float* __restrict__ u_rec, TIn* __restrict__ kg_rec, int32_t* __restrict__ dev_err) {
-  // per position of the block: D_t k, D_t q (for the dots), k / D_t (update), v
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int EP = 16 / (int)sizeof(TIn);   // input elements per 16-byte piece
+  constexpr int PPR = kD / EP;                 // pieces per 128-element row
+  // per position of the block: D_t k, D_t q (for the dots), k / D_t (update)
   __shared__ __align__(16) float s_wk[kTB][kD];
   __shared__ __align__(16) float s_wq[kTB][kD];
   __shared__ __align__(16) float s_ku[kTB][kD];
-  __shared__ __align__(16) float s_v[kTB][kD];
   __shared__ __align__(16) float s_dec[kD];      // D at the end of the block
   __shared__ float s_beta[kTB], s_kq[2][kTB];    // k . q as two 64-channel halves
+  // the block's inputs as loaded (rows of 128: k, g, q, v), and its outputs
+  // u and o, so that every global access moves 16 bytes per lane
+  __shared__ __align__(16) TIn s_in[4][kTB][kD];
+  __shared__ __align__(16) float s_u[kTB][kD];
+  __shared__ __align__(16) TIn s_o[kTB][kD];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -75,27 +82,40 @@ __global__ __launch_bounds__(kT) void kda_verify_kernel(
     for (int j = 0; j < 4; ++j) S[i][j] = load4(src + (row0 + i) * kD + 4 * gl + 32 * j);
 
   const int64_t tok_stride = (int64_t)H * kD;
+  const TIn* const arr[4] = {k, g, q, v};
+  TIn* const kg_rh = kg_rec + ((int64_t)r * H + h) * L * (2 * kD);   // [L][2 kD] of this (req, head)
+  float* const u_rh = u_rec + ((int64_t)r * H + h) * L * kD;        // [L][kD]
   for (int t0 = 0; t0 < L; t0 += kTB) {
     const int nb = min(kTB, L - t0);
     if (t0 > 0) __syncthreads();  // every wave is done with the previous block
-    // ---- per-position vectors: threads 0..127 own one key channel each and
-    //      run the cumulative decay over the block; threads 128..255 load v
-    //      and beta.  Loads past the block end are clamped to its last
-    //      position (branch-free, so they all issue before the first use).
-    if (tid < kD) {
-      TIn kr[kTB], gr[kTB], qr[kTB];
+    // ---- stage the block's rows: piece p = (array, position, part); rows
+    //      past the block end repeat its last position
 #pragma unroll
-      for (int jj = 0; jj < kTB; ++jj) {
-        const int64_t base = ((int64_t)r * L + t0 + min(jj, nb - 1)) * tok_stride + (int64_t)h * kD + tid;
-        kr[jj] = k[base];
-        gr[jj] = g[base];
-        qr[jj] = q[base];
-      }
+    for (int pp = 0; pp < 4 * kTB * PPR / kT; ++pp) {
+      const int pc = tid + kT * pp;
+      const int a = pc / (kTB * PPR), jj = (pc / PPR) % kTB, part = pc % PPR;
+      const int64_t off = ((int64_t)r * L + t0 + min(jj, nb - 1)) * tok_stride + (int64_t)h * kD + part * EP;
+      *reinterpret_cast<u32x4*>(&s_in[a][jj][part * EP]) = *reinterpret_cast<const u32x4*>(arr[a] + off);
+    }
+    if (tid < kTB) s_beta[tid] = sigmoidf_(to_f32(bl[((int64_t)r * L + t0 + min(tid, nb - 1)) * H + h]));
+    __syncthreads();
+    // ---- records of k and the raw gate: [position][k | g], contiguous
+#pragma unroll
+    for (int pp = 0; pp < 2 * kTB * PPR / kT; ++pp) {
+      const int pc = tid + kT * pp;
+      const int jj = pc / (2 * PPR), a = (pc / PPR) % 2, part = pc % PPR;
+      if (jj < nb)
+        *reinterpret_cast<u32x4*>(kg_rh + (int64_t)(t0 + jj) * (2 * kD) + a * kD + part * EP) =
+            *reinterpret_cast<const u32x4*>(&s_in[a][jj][part * EP]);
+    }
+    // ---- per-position vectors: threads 0..127 own one key channel each and
+    //      run the cumulative decay over the block
+    if (tid < kD) {
       float D = 1.f;
 #pragma unroll
       for (int jj = 0; jj < kTB; ++jj) {
-        const float kk = to_f32(kr[jj]), qq = to_f32(qr[jj]);
-        D *= __expf(to_f32(gr[jj]));
+        const float kk = to_f32(s_in[0][jj][tid]), qq = to_f32(s_in[2][jj][tid]);
+        D *= __expf(to_f32(s_in[1][jj][tid]));
         s_wk[jj][tid] = D * kk;
         s_wq[jj][tid] = D * qq;
         s_ku[jj][tid] = kk / D;
@@ -103,28 +123,12 @@ __global__ __launch_bounds__(kT) void kda_verify_kernel(
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) p += __shfl_xor(p, m);
         if (lane == 0) s_kq[wave][jj] = p;
-        if (jj < nb) {
-          TIn* rec = kg_rec + (((int64_t)r * H + h) * L + t0 + jj) * (2 * kD);
-          rec[tid] = kr[jj];
-          rec[kD + tid] = gr[jj];
-        }
       }
       s_dec[tid] = D;  // read only when the block is full (a next block exists)
-    } else {
-      const int c = tid - kD;
-      TIn vr[kTB];
-#pragma unroll
-      for (int jj = 0; jj < kTB; ++jj)
-        vr[jj] = v[((int64_t)r * L + t0 + min(jj, nb - 1)) * tok_stride + (int64_t)h * kD + c];
-      const TIn br = bl[((int64_t)r * L + t0 + min(c, nb - 1)) * H + h];
-#pragma unroll
-      for (int jj = 0; jj < kTB; ++jj) s_v[jj][c] = to_f32(vr[jj]);
-      if (c < kTB) s_beta[c] = sigmoidf_(to_f32(br));
     }
     __syncthreads();
 
     for (int jj = 0; jj < nb; ++jj) {
-      const int t = t0 + jj;
       floatx4 wk[4], wq[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -148,16 +152,16 @@ __global__ __launch_bounds__(kT) void kda_verify_kernel(
       const float beta = s_beta[jj], kqv = s_kq[0][jj] + s_kq[1][jj];
       float u[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) u[i] = beta * (s_v[jj][row0 + i] - pred[i]);
-      // lanes 0..3 of a group write u and lanes 4..7 write o, one row each
+      for (int i = 0; i < 4; ++i) u[i] = beta * (to_f32(s_in[3][jj][row0 + i]) - pred[i]);
+      // lanes 0..3 of a group hold u and lanes 4..7 o, one row each
       {
         const int i = gl & 3;
         const float ui = (i == 0) ? u[0] : (i == 1) ? u[1] : (i == 2) ? u[2] : u[3];
         const float oqi = (i == 0) ? oq[0] : (i == 1) ? oq[1] : (i == 2) ? oq[2] : oq[3];
-        if (gl < 4) u_rec[(((int64_t)r * H + h) * L + t) * kD + row0 + i] = ui;
-        else o[((int64_t)r * L + t) * tok_stride + (int64_t)h * kD + row0 + i] = from_f32<TIn>(oqi + ui * kqv);
+        if (gl < 4) s_u[jj][row0 + i] = ui;
+        else s_o[jj][row0 + i] = from_f32<TIn>(oqi + ui * kqv);
       }
-      if (t + 1 < L) {
+      if (t0 + jj + 1 < L) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const floatx4 ku = *reinterpret_cast<const floatx4*>(&s_ku[jj][4 * gl + 32 * j]);
@@ -174,6 +178,22 @@ __global__ __launch_bounds__(kT) void kda_verify_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[i][j] = d4 * S[i][j];
       }
+    }
+    __syncthreads();
+    // ---- the block's u (fp32, contiguous per (req, head)) and o rows
+#pragma unroll
+    for (int pp = 0; pp < kTB * kD / 4 / kT; ++pp) {
+      const int pc = tid + kT * pp;
+      const int jj = pc / (kD / 4), part = pc % (kD / 4);
+      if (jj < nb)
+        *reinterpret_cast<u32x4*>(u_rh + (int64_t)(t0 + jj) * kD + 4 * part) =
+            *reinterpret_cast<const u32x4*>(&s_u[jj][4 * part]);
+    }
+    for (int pc = tid; pc < kTB * PPR; pc += kT) {
+      const int jj = pc / PPR, part = pc % PPR;
+      if (jj < nb)
+        *reinterpret_cast<u32x4*>(o + ((int64_t)r * L + t0 + jj) * tok_stride + (int64_t)h * kD + part * EP) =
+            *reinterpret_cast<const u32x4*>(&s_o[jj][part * EP]);
     }
   }
 }

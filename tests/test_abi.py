@@ -110,6 +110,8 @@ def test_verify_commit_copy_host_errors(L):
     assert v(o=None) == 1
     assert v(n=-1) == 1
     assert v(pool=pool(H=4)) == 1
+    for name in ("q", "k", "v", "g", "o", "u", "kg"):   # every streamed buffer must be 16-byte aligned
+        assert v(**{name: ctypes.c_void_p(FAKE.value + 8)}) == 1
     assert v(n=0) == 0
     c = lambda **kw: L.kda_commit(*[kw.get(n, d) for n, d in [
         ("pool", P), ("ck", FAKE), ("dst", None), ("acc", FAKE), ("u", FAKE), ("kg", FAKE),
