@@ -136,6 +136,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="extra steps, each after a 512 MiB cache-flushing write (0 to skip)")
     ap.add_argument("--traffic-calibration", action="store_true",
                     help="after the timed steps, run one kda_state_copy of 256 distinct fp32 "
                          "slots (512 MiB read + 512 MiB written) so that FETCH_SIZE / WRITE_SIZE "
@@ -182,14 +184,33 @@ def main():
         step(evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = {c: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(a.steps)]))
-          for i, c in enumerate(calls)}
+    per = {c: np.array([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(a.steps)])
+           for i, c in enumerate(calls)}
+    ms = {c: float(per[c].mean()) for c in calls}
     ms_step = wall / a.steps * 1e3
+    # Second pass, not part of `value`: a 512 MiB scratch write between steps
+    # (outside the per-call events) evicts L2 and the MALL, so every call
+    # starts with its inputs in HBM only.
+    cold = None
+    if a.cold_steps > 0:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cevs = [[ev() for _ in range(5)] for _ in range(a.cold_steps)]
+        for s in range(a.cold_steps):
+            scratch.fill_(s & 0xFF)
+            step(cevs[s])
+        torch.cuda.synchronize()
+        cold = {c: np.array([cevs[s][i].elapsed_time(cevs[s][i + 1]) for s in range(a.cold_steps)])
+                for i, c in enumerate(calls)}
+        del scratch
     if a.traffic_calibration:
         ck = sp["case"]["ckpt_slots"]
         fresh = sorted(set(range(sp["case"]["n_slots"])) - set(ck.tolist()))[:len(ck)]
         kda.state_copy(sp["pool"], i32(ck, dev), i32(fresh, dev))
         torch.cuda.synchronize()
+
+    def spread(x):
+        return {"median": float(np.median(x)), "p10": float(np.percentile(x, 10)),
+                "p90": float(np.percentile(x, 90))}
 
     p_s = ms["prefill"] * 1e-3
     tokens_per_s = T / p_s
@@ -214,13 +235,19 @@ def main():
         "config": {"workload": "single-layer KDA prefill T=8229 H=32 d_k=d_v=128 chunk=64 bf16 "
                                "fp32-pool + spec-decode verify/commit/fork n_req=256 L=8 H=32",
                    "global_batch": 1, "seq_len": T, "heads": 32, "head_dim": 128, "chunk": 64},
-        "prefill": {"ms": ms["prefill"], "tokens_per_s": tokens_per_s,
+        "prefill": {"ms": ms["prefill"], "ms_spread": spread(per["prefill"]), "tokens_per_s": tokens_per_s,
                     "hbm_GBps": p_bytes / p_s / 1e9, "hbm_frac": p_bytes / p_s / HBM_PEAK,
                     "mfma_TFLOPs": p_flops / p_s / 1e12, "mfma_frac": p_flops / p_s / BF16_PEAK},
-        "verify": {"ms": ms["verify"], "GBps": gbs["verify"], "hbm_frac": gbs["verify"] * 1e9 / HBM_PEAK},
-        "commit": {"ms": ms["commit"], "GBps": gbs["commit"], "hbm_frac": gbs["commit"] * 1e9 / HBM_PEAK},
-        "copy": {"ms": ms["copy"], "GBps": gbs["copy"], "hbm_frac": gbs["copy"] * 1e9 / HBM_PEAK},
+        "verify": {"ms": ms["verify"], "ms_spread": spread(per["verify"]), "GBps": gbs["verify"], "hbm_frac": gbs["verify"] * 1e9 / HBM_PEAK},
+        "commit": {"ms": ms["commit"], "ms_spread": spread(per["commit"]), "GBps": gbs["commit"], "hbm_frac": gbs["commit"] * 1e9 / HBM_PEAK},
+        "copy": {"ms": ms["copy"], "ms_spread": spread(per["copy"]), "GBps": gbs["copy"], "hbm_frac": gbs["copy"] * 1e9 / HBM_PEAK},
         "roofline": roof,
+        "cold": None if cold is None else {
+            "note": "L2 and MALL flushed by a 512 MiB write before each step",
+            "steps": a.cold_steps,
+            **{c: {"ms_median": float(np.median(cold[c])), "ms_p10": float(np.percentile(cold[c], 10)),
+                   "ms_p90": float(np.percentile(cold[c], 90))} for c in calls},
+            "prefill_tokens_per_s": T / (float(np.median(cold["prefill"])) * 1e-3)},
         "device": torch.cuda.get_device_name(0),
     }
     if not a.no_cpu_baseline:
