@@ -95,7 +95,7 @@ def measured_prefill_traffic():
     prefill sources changed since those counters were taken."""
     import hashlib
     h = hashlib.sha256()
-    for name in ("prefill.hip", "kda_common.hpp", "kda_launch.hpp"):
+    for name in ("prefill.hip", "prefill16.hip", "prefill_common.hpp", "kda_common.hpp", "kda_launch.hpp"):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     try:

@@ -37,82 +37,9 @@
 //     XCD's L2.
 #include <type_traits>
 
-#include "kda_common.hpp"
-#include "kda_launch.hpp"
+#include "prefill_common.hpp"
 
 namespace kda {
-
-constexpr int kThreads = 256;
-constexpr int kXcd = 8;     // MI355X: workgroups are dealt round-robin to 8 XCDs
-constexpr int kFB = 1024;   // bytes of one fragment block: 64 lanes x 16 bytes
-constexpr int kNumCU = 256; // MI355X compute units
-constexpr int kSpreadLds = 72 * 1024;  // with the static part, > half of a CU's 160 KiB LDS
-
-// K-block sizes: 32 for the 16-bit 16x16x32 MFMAs; fp32 uses 16 so that one
-// lane's fragment is 16 bytes as well.
-template <typename TOp> struct KBOf { static constexpr int v = (sizeof(TOp) == 4) ? 16 : 32; };
-
-// Workspace record for one (chunk, head).  A-operand matrices are stored as
-// fragment blocks: block (tile, kb) of an M x K matrix holds, for lane
-// l = 16 g + r, row 16 tile + r at K-block positions kb*KB + (KB/4) g + j.
-template <int DK, int C, typename TOp>
-struct Rec {
-  static constexpr int KBK = KBOf<TOp>::v, KBT = KBOf<TOp>::v;
-  static constexpr int NBK = (C / 16) * (DK / KBK);   // Kt and Qt blocks   (tile = token tile)
-  static constexpr int NBB = (DK / 16) * (C / KBT);   // Kb^T blocks        (tile = key tile)
-  static constexpr int NBT = (C / 16) * (C / KBT);    // T and P blocks     (tile = token tile)
-  static constexpr int kKt = 0;
-  static constexpr int kQt = kKt + NBK * kFB;
-  static constexpr int kKbT = kQt + NBK * kFB;
-  static constexpr int kT = kKbT + NBB * kFB;
-  static constexpr int kP = kT + NBT * kFB;
-  static constexpr int kBeta = kP + NBT * kFB;          // [C]  fp32
-  static constexpr int kDec = kBeta + C * 4;            // [DK] fp32, e^Gamma_n
-  static constexpr int kEnd = kDec + DK * 4;
-  static constexpr int kBytes = (kEnd + 255) / 256 * 256;
-  static_assert((KBK / 4) * sizeof(TOp) == 16, "16-byte fragments");
-  static_assert(DK % KBK == 0 && C % KBT == 0, "tile sizes");
-};
-
-__host__ __device__ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
-__host__ __device__ inline int64_t map_bytes(int n_seqs) { return round_up(4 * (int64_t)(n_seqs + 1), 256); }
-__host__ __device__ inline int64_t chunk_upper_bound(int64_t total_tokens, int n_seqs, int C) {
-  return total_tokens / C + n_seqs;
-}
-
-// Inverse of pos_in_block: index stored at position p of a K-block.
-template <int KB>
-__device__ __forceinline__ int idx_in_block(int p) {
-  if (KB == 16) return p;
-  const int g = p >> 3, j = p & 7;
-  return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
-}
-
-// A sequence is processed only if its cu_seqlens entries are sane and the
-// chunk map gave it exactly ceil(len / C) chunks.
-__device__ __forceinline__ bool seq_ok(const int32_t* cu, const int32_t* off, int seq,
-                                       int64_t total, int C, int& t_beg, int& len, int& nch) {
-  t_beg = cu[seq];
-  const int t_end = cu[seq + 1];
-  len = t_end - t_beg;
-  nch = (len + C - 1) / C;
-  return t_beg >= 0 && len >= 0 && (int64_t)t_end <= total && off[seq + 1] - off[seq] == nch;
-}
-
-// 16 bytes viewed as a fragment of TOp elements.
-template <typename TOp>
-union Frag16 {
-  uint4 u;
-  TOp e[16 / sizeof(TOp)];
-};
-
-template <typename F>
-__device__ __forceinline__ F as_frag(const uint4& x) {
-  static_assert(sizeof(F) == 16, "fragment size");
-  F f;
-  __builtin_memcpy(&f, &x, 16);
-  return f;
-}
 
 // ---------------------------------------------------------------- 1. chunk map
 
@@ -433,379 +360,6 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_prep(
   }
 }
 
-// ---------------------------------------------------------------- 2b. prep, 16-bit operands
-//
-// One workgroup per (chunk, head), four waves; wave w owns token tile w
-// (tokens 16w .. 16w+15 of the chunk), and lane l = 16 g + r holds token
-// 16w + r at the channel positions that make up its MFMA fragment (channels
-// 32kb + 4g + e and 32kb + 16 + 4g + e of every 32-channel block kb), so
-// Kt and Qt leave registers as fragment blocks directly.
-//   * cumulative log decay Gamma along the chunk: prefix sums over the 16
-//     lanes of a row (DPP), carried across token tiles through LDS;
-//     exp(Gamma) and exp(Gamma_n - Gamma) are the two exponentials per
-//     element; e^-Gamma = e^(Gamma_n - Gamma) e^-Gamma_n.
-//   * Kb^T: each 16 x 16 tile is transposed by one MFMA against a 0/1
-//     selection matrix (exact: bf16 values times 1, summed with zeros).
-//   * P = Qt Kh^T and M = Kt Kh^T are computed transposed (Kh as the A
-//     operand), which puts them in the registers in fragment order: the
-//     accumulator of P^T tile (j, i) is the j-th half of P's fragment row i.
-//   * T = (I + Diag(beta) strict_tril(M))^-1 by 16 x 16 blocks: each wave
-//     inverts its diagonal block as (I - N)(I + N^2)(I + N^4)(I + N^8)
-//     (N is nilpotent), then wave j walks down block column j,
-//     T_ij = -T_ii sum_{m=j}^{i-1} N_im T_mj.  These fp32 products run as
-//     three bf16 MFMAs on a hi/lo split of both factors.
-typedef short short4v __attribute__((ext_vector_type(4)));
-
-// A 16 x 16 fp32 tile in one of two register forms, for lane l = 16 g + r:
-//   row form:    X[r][4g + e]   (the A operand of a 16x16x16 product)
-//   column form: X[4g + e][r]   (the B operand, and the accumulator layout)
-// The row form of X holds the numbers of the column form of X^T.
-struct Split { short4v hi, lo; };
-
-__device__ __forceinline__ Split split_bf16(floatx4 x) {
-  Split s;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const bf16 h = (bf16)x[e];
-    const bf16 l = (bf16)(x[e] - (float)h);
-    s.hi[e] = __builtin_bit_cast(short, h);
-    s.lo[e] = __builtin_bit_cast(short, l);
-  }
-  return s;
-}
-// column form of A B, given A in row form and B in column form
-__device__ __forceinline__ floatx4 mm16(const Split& a, const Split& b) {
-  floatx4 c = {0.f, 0.f, 0.f, 0.f};
-  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.hi, c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.lo, c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b.hi, c, 0, 0, 0);
-  return c;
-}
-__device__ __forceinline__ floatx4 plus_eye(floatx4 x, int g, int r) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) x[e] += (4 * g + e == r) ? 1.f : 0.f;
-  return x;
-}
-__device__ __forceinline__ float row_shr(float x, int s) {
-  // value of the lane s places lower in the same 16-lane row, 0 past its start
-  int v = __builtin_bit_cast(int, x);
-  switch (s) {
-    case 1: v = __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true); break;
-    case 2: v = __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true); break;
-    case 4: v = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true); break;
-    default: v = __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true); break;
-  }
-  return __builtin_bit_cast(float, v);
-}
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-struct Prep16Smem {
-  float tot[4][128];          // per token tile: sum of g over the tile
-  float off[4][128];          // sum of g over the preceding tiles
-  float gn[128], ninv[128];   // Gamma_n, e^-Gamma_n
-  uint4 kh[4][4][64];         // Kh fragments, [token tile][channel block][lane]
-  float nd[4][16][20];        // diagonal N blocks, row-major (for the column form)
-  floatx4 nr[6][64];          // row forms of N_im, m < i, at i (i - 1) / 2 + m
-  floatx4 dr[4][64];          // row forms of T_ii
-};
-
-template <typename TIn, typename TOp>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void kda_chunk_prep16(
-    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ g,
-    const TIn* __restrict__ bl, const int32_t* __restrict__ cu, int n_seqs, int64_t total,
-    int H, int64_t cap, const int32_t* __restrict__ off, uint8_t* __restrict__ recs) {
-  constexpr int DK = 128, C = 64;
-  typedef Rec<DK, C, TOp> R;
-  typedef typename OpTraits<TOp>::frag F8;   // 8 x 16-bit fragment
-  typedef typename Vec4<TIn>::type In4;
-  constexpr int NFK = DK / 32, NFT = C / 32;
-  static_assert(R::KBK == 32 && R::KBT == 32, "16-bit operand layout");
-  __shared__ Prep16Smem sm;
-
-  const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, r = lane & 15;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // token tile, wave-uniform
-  const int h = blockIdx.x % H;
-  const int j = blockIdx.x / H;  // global chunk slot
-  if (j >= off[n_seqs]) return;
-  int lo = 0, hi = n_seqs - 1;   // sequence owning chunk slot j
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (off[mid] <= j) lo = mid; else hi = mid - 1;
-  }
-  int t_beg, len, nch;
-  if (!seq_ok(cu, off, lo, total, C, t_beg, len, nch)) return;
-  const int c = j - off[lo];
-  if (c >= nch) return;
-  const int t0 = t_beg + c * C;
-  const int n = min(C, len - c * C);
-  uint8_t* rec = recs + ((int64_t)h * cap + j) * R::kBytes;
-
-  // ---- inputs of this lane's token (rows past the chunk's end: clamped
-  //      loads, masked values)
-  const int t = 16 * w + r;
-  const bool valid = t < n;
-  const int64_t row = (int64_t)(t0 + min(t, n - 1));
-  const int64_t base = row * H * DK + (int64_t)h * DK + 4 * gq;
-  In4 kr[NFK][2], qr[NFK][2], grw[NFK][2];
-#pragma unroll
-  for (int kb = 0; kb < NFK; ++kb)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int64_t o = base + 32 * kb + 16 * hf;
-      kr[kb][hf] = *reinterpret_cast<const In4*>(k + o);
-      qr[kb][hf] = *reinterpret_cast<const In4*>(q + o);
-      grw[kb][hf] = *reinterpret_cast<const In4*>(g + o);
-    }
-  const float beta = valid ? sigmoidf_(to_f32(bl[row * H + h])) : 0.f;
-  if (gq == 0) reinterpret_cast<float*>(rec + R::kBeta)[t] = beta;
-
-  // ---- Gamma: prefix sums of g over the tile's 16 tokens (DPP), then the
-  //      tile totals go through LDS to give every tile its offset
-  float gs[NFK][8];
-#pragma unroll
-  for (int kb = 0; kb < NFK; ++kb)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) gs[kb][e] = valid ? to_f32(grw[kb][e >> 2][e & 3]) : 0.f;
-#pragma unroll
-  for (int s = 1; s < 16; s <<= 1)
-#pragma unroll
-    for (int kb = 0; kb < NFK; ++kb)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) gs[kb][e] += row_shr(gs[kb][e], s);
-  if (r == 15) {
-#pragma unroll
-    for (int kb = 0; kb < NFK; ++kb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-        *reinterpret_cast<floatx4*>(&sm.tot[w][32 * kb + 16 * hf + 4 * gq]) =
-            floatx4{gs[kb][4 * hf], gs[kb][4 * hf + 1], gs[kb][4 * hf + 2], gs[kb][4 * hf + 3]};
-  }
-  __syncthreads();
-  if (w == 0) {
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const int ch = lane + 64 * cc;
-      const float a0 = sm.tot[0][ch], a1 = sm.tot[1][ch], a2 = sm.tot[2][ch], a3 = sm.tot[3][ch];
-      sm.off[0][ch] = 0.f;
-      sm.off[1][ch] = a0;
-      sm.off[2][ch] = a0 + a1;
-      sm.off[3][ch] = a0 + a1 + a2;
-      const float gn = a0 + a1 + a2 + a3;
-      sm.gn[ch] = gn;
-      sm.ninv[ch] = __expf(-gn);
-      reinterpret_cast<float*>(rec + R::kDec)[ch] = __expf(gn);
-    }
-  }
-  __syncthreads();
-
-  // ---- Kt = K e^Gamma, Qt = Q e^Gamma, Kb = K e^(Gamma_n - Gamma), Kh = Kb e^-Gamma_n
-  F8 ktf[NFK], qtf[NFK], kbf[NFK], khf[NFK];
-#pragma unroll
-  for (int kb = 0; kb < NFK; ++kb)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int ch = 32 * kb + 16 * hf + 4 * gq;
-      const floatx4 of = *reinterpret_cast<const floatx4*>(&sm.off[w][ch]);
-      const floatx4 gn = *reinterpret_cast<const floatx4*>(&sm.gn[ch]);
-      const floatx4 ni = *reinterpret_cast<const floatx4*>(&sm.ninv[ch]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float G = gs[kb][4 * hf + e] + of[e];
-        const float a = __expf(G), b = __expf(gn[e] - G);
-        const float kv = valid ? to_f32(kr[kb][hf][e]) : 0.f;
-        const float qv = valid ? to_f32(qr[kb][hf][e]) : 0.f;
-        const float kbv = kv * b;
-        ktf[kb][4 * hf + e] = from_f32<TOp>(kv * a);
-        qtf[kb][4 * hf + e] = from_f32<TOp>(qv * a);
-        kbf[kb][4 * hf + e] = from_f32<TOp>(kbv);
-        khf[kb][4 * hf + e] = from_f32<TOp>(kbv * ni[e]);
-      }
-    }
-#pragma unroll
-  for (int kb = 0; kb < NFK; ++kb) {
-    *reinterpret_cast<F8*>(rec + R::kKt + (w * NFK + kb) * kFB + lane * 16) = ktf[kb];
-    *reinterpret_cast<F8*>(rec + R::kQt + (w * NFK + kb) * kFB + lane * 16) = qtf[kb];
-    sm.kh[w][kb][lane] = __builtin_bit_cast(uint4, khf[kb]);
-  }
-  // Kb^T: transpose each 16-token x 16-channel tile with one MFMA against a
-  // 0/1 selection of the channel half hf; the accumulator (token rows
-  // 4g+e, channel column r) is half (w % 2) of Kb^T's fragment entry.
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    F8 sel;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int idx = p < 4 ? 4 * gq + p : 16 + 4 * gq + (p - 4);  // channel index at position 8g+p
-      sel[p] = from_f32<TOp>(idx == 16 * hf + r ? 1.f : 0.f);
-    }
-#pragma unroll
-    for (int kb = 0; kb < NFK; ++kb) {
-      const floatx4 tr = mma(floatx4{0.f, 0.f, 0.f, 0.f}, kbf[kb], sel);
-      typename Vec4<TOp>::type o4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = from_f32<TOp>(tr[e]);
-      *reinterpret_cast<typename Vec4<TOp>::type*>(
-          rec + R::kKbT + ((2 * kb + hf) * NFT + (w >> 1)) * kFB + lane * 16 + 8 * (w & 1)) = o4;
-    }
-  }
-  __syncthreads();
-
-  // ---- P^T and M^T tiles (j, w) for j <= w: Kh of tile j is the A operand,
-  //      this tile's Qt / Kt fragments serve as the B operand.  Lane (g, r)
-  //      then holds P[16w + r][16j + 4g + e], the row form of P_wj.
-  floatx4 ptile[4], nrow[4];
-  const int rr = 16 * w + r;  // this lane's row of P, M, N, T
-#pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
-    ptile[jt] = nrow[jt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (jt > w) continue;
-    floatx4 pm = {0.f, 0.f, 0.f, 0.f}, pp = pm;
-#pragma unroll
-    for (int kb = 0; kb < NFK; ++kb) {
-      const F8 a = __builtin_bit_cast(F8, sm.kh[jt][kb][lane]);
-      pm = mma(pm, a, ktf[kb]);
-      pp = mma(pp, a, qtf[kb]);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int s = 16 * jt + 4 * gq + e;
-      ptile[jt][e] = s <= rr ? pp[e] : 0.f;
-      nrow[jt][e] = s < rr ? beta * pm[e] : 0.f;
-    }
-  }
-  // P fragments: block (w, kb) = [P_w,2kb | P_w,2kb+1] (upper halves zero)
-#pragma unroll
-  for (int kb = 0; kb < NFT; ++kb) {
-    if (kb > w / 2) continue;  // K-blocks up to the diagonal
-    F8 pf;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pf[e] = from_f32<TOp>(ptile[2 * kb][e]);
-      pf[4 + e] = from_f32<TOp>(ptile[2 * kb + 1][e]);
-    }
-    *reinterpret_cast<F8*>(rec + R::kP + (w * NFT + kb) * kFB + lane * 16) = pf;
-  }
-
-  // ---- T_ww = (I + N_ww)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8), both forms
-  const floatx4 n1r = nrow[w];
-  *reinterpret_cast<floatx4*>(&sm.nd[w][r][4 * gq]) = n1r;
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-    if (m < w) sm.nr[w * (w - 1) / 2 + m][lane] = nrow[m];
-  wave_sync();
-  floatx4 n1c;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) n1c[e] = sm.nd[w][4 * gq + e][r];
-  const Split s1r = split_bf16(n1r), s1c = split_bf16(n1c);
-  const floatx4 n2c = mm16(s1r, s1c), n2r = mm16(s1c, s1r);
-  const Split s2r = split_bf16(n2r), s2c = split_bf16(n2c);
-  const floatx4 n4c = mm16(s2r, s2c), n4r = mm16(s2c, s2r);
-  const Split s4r = split_bf16(n4r), s4c = split_bf16(n4c);
-  const floatx4 n8c = mm16(s4r, s4c), n8r = mm16(s4c, s4r);
-  floatx4 dc = plus_eye(n8c, gq, r);
-  dc = dc + mm16(s4r, split_bf16(dc));
-  dc = dc + mm16(s2r, split_bf16(dc));
-  dc = dc - mm16(s1r, split_bf16(dc));        // column form of T_ww
-  floatx4 dr = plus_eye(n8r, gq, r);
-  dr = dr + mm16(s4c, split_bf16(dr));
-  dr = dr + mm16(s2c, split_bf16(dr));
-  dr = dr - mm16(s1c, split_bf16(dr));        // row form of T_ww
-  sm.dr[w][lane] = dr;
-  {
-    // T block (w, w/2): this half is T_ww; for even w the other half
-    // (T_w,w+1) is zero
-    typename Vec4<TOp>::type o4;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o4[e] = from_f32<TOp>(dr[e]);
-    uint8_t* dst = rec + R::kT + (w * NFT + (w >> 1)) * kFB + lane * 16;
-    if (w & 1) {
-      *reinterpret_cast<typename Vec4<TOp>::type*>(dst + 8) = o4;
-    } else {
-      F8 f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { f[e] = o4[e]; f[4 + e] = from_f32<TOp>(0.f); }
-      *reinterpret_cast<F8*>(dst) = f;
-    }
-  }
-  __syncthreads();
-
-  // ---- block column w: T_iw = -T_ii sum_{m=w}^{i-1} N_im T_mw, i > w
-  floatx4 tc[4];
-  tc[0] = tc[1] = tc[2] = tc[3] = floatx4{0.f, 0.f, 0.f, 0.f};
-  tc[w] = dc;
-#pragma unroll
-  for (int i = 1; i < 4; ++i) {
-    if (i <= w) continue;
-    floatx4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < 3; ++m)
-      if (m >= w && m < i) z = z + mm16(split_bf16(sm.nr[i * (i - 1) / 2 + m][lane]), split_bf16(tc[m]));
-    const Split szc = split_bf16(z), sdr = split_bf16(sm.dr[i][lane]);
-    tc[i] = -mm16(sdr, szc);                   // column form, feeds the next rows
-    const floatx4 trow = -mm16(szc, sdr);      // row form: T[16i + r][16w + 4g + e]
-    typename Vec4<TOp>::type o4;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o4[e] = from_f32<TOp>(trow[e]);
-    *reinterpret_cast<typename Vec4<TOp>::type*>(
-        rec + R::kT + (i * NFT + (w >> 1)) * kFB + lane * 16 + 8 * (w & 1)) = o4;
-  }
-}
-
-// ---------------------------------------------------------------- 3. scan
-
-template <typename T>
-__device__ __forceinline__ T bits_to(uint32_t b) {
-  if constexpr (sizeof(T) == 2) {
-    const uint16_t h = (uint16_t)b;
-    T x;
-    __builtin_memcpy(&x, &h, 2);
-    return x;
-  } else {
-    T x;
-    __builtin_memcpy(&x, &b, 4);
-    return x;
-  }
-}
-template <typename T>
-__device__ __forceinline__ uint32_t to_bits(T x) {
-  if constexpr (sizeof(T) == 2) {
-    uint16_t h;
-    __builtin_memcpy(&h, &x, 2);
-    return h;
-  } else {
-    uint32_t b;
-    __builtin_memcpy(&b, &x, 4);
-    return b;
-  }
-}
-__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-  return uint4{(unsigned)x[0], (unsigned)x[1], (unsigned)x[2], (unsigned)x[3]};
-}
-__device__ __forceinline__ floatx4 ld16f(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-  floatx4 f;
-  __builtin_memcpy(&f, &x, 16);
-  return f;
-}
-
-// K-blocks of T and P rows of token tile mt up to the diagonal, and the
-// index of block (mt, 0) among the lower (incl. diagonal) T blocks.
-template <int KB>
-__host__ __device__ constexpr int scan_nkb(int mt) { return (16 * mt + 15) / KB + 1; }
-template <int KB>
-__host__ __device__ constexpr int scan_tblk(int mt) {
-  int j = 0;
-  for (int m = 0; m < mt; ++m) j += scan_nkb<KB>(m);
-  return j;
-}
-
-// Scan geometry: four waves per (sequence, head, 16-column tile of S).
-// Wave w owns token tile w (rows of X, Y, O) and S K-block w (key tiles
 // w*KB/16 ...), so it loads only its own quarter of each record.
 template <int DK, int C, typename TOp>
 struct ScanGeom {
@@ -1131,48 +685,43 @@ __global__ __launch_bounds__(256) void kda_chunk_scan(
 
 namespace {
 
+struct WsView {
+  int64_t cap;     // chunk slots per head
+  int32_t* off;    // per-sequence chunk offsets (the chunk map)
+  uint8_t* recs;   // records, [head][chunk slot]
+};
+
+WsView map_chunks(const PrefillArgs& a, hipStream_t st, int C) {
+  WsView w;
+  w.cap = chunk_upper_bound(a.total_tokens, a.n_seqs, C);
+  uint8_t* ws = static_cast<uint8_t*>(a.workspace);
+  w.off = reinterpret_cast<int32_t*>(ws);
+  w.recs = ws + map_bytes(a.n_seqs);
+  hipLaunchKernelGGL(kda_chunk_map, dim3(1), dim3(kThreads), 0, st, a.cu_seqlens, a.n_seqs,
+                     a.total_tokens, C, w.cap, w.off, a.dev_err);
+  return w;
+}
+
 template <int DK, int DV, int C, typename TIn, typename TOp, typename TPool>
 hipError_t run(const PrefillArgs& a, hipStream_t st) {
   typedef PrepSmem<DK, C, TOp> SmP;
-  const int64_t cap = chunk_upper_bound(a.total_tokens, a.n_seqs, C);
-  uint8_t* ws = static_cast<uint8_t*>(a.workspace);
-  int32_t* off = reinterpret_cast<int32_t*>(ws);
-  uint8_t* recs = ws + map_bytes(a.n_seqs);
-
-  hipLaunchKernelGGL(kda_chunk_map, dim3(1), dim3(kThreads), 0, st, a.cu_seqlens, a.n_seqs,
-                     a.total_tokens, C, cap, off, a.dev_err);
-  if (cap > 0) {
-    if constexpr (sizeof(TOp) == 2) {
-      hipLaunchKernelGGL((kda_chunk_prep16<TIn, TOp>), dim3((unsigned)(cap * a.H)), dim3(kThreads), 0, st,
-                         static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
-                         static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.b), a.cu_seqlens,
-                         a.n_seqs, a.total_tokens, a.H, cap, off, recs);
-    } else {
-      auto kp = kda_chunk_prep<DK, C, TIn, TOp>;
-      const int smp = (int)sizeof(SmP);
-      hipError_t e = hipFuncSetAttribute((const void*)kp, hipFuncAttributeMaxDynamicSharedMemorySize, smp);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(kp, dim3((unsigned)(cap * a.H)), dim3(kThreads), smp, st,
-                         static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
-                         static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.b), a.cu_seqlens,
-                         a.n_seqs, a.total_tokens, a.H, cap, off, recs);
-    }
+  const WsView w = map_chunks(a, st, C);
+  if (w.cap > 0) {
+    auto kp = kda_chunk_prep<DK, C, TIn, TOp>;
+    const int smp = (int)sizeof(SmP);
+    hipError_t e = hipFuncSetAttribute((const void*)kp, hipFuncAttributeMaxDynamicSharedMemorySize, smp);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kp, dim3((unsigned)(w.cap * a.H)), dim3(kThreads), smp, st,
+                       static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
+                       static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.b), a.cu_seqlens,
+                       a.n_seqs, a.total_tokens, a.H, w.cap, w.off, w.recs);
   }
   auto ks = kda_chunk_scan<DK, DV, C, TIn, TOp, TPool>;
   const int64_t pairs = (int64_t)a.n_seqs * a.H;
   const int64_t blocks = (pairs + kXcd - 1) / kXcd * kXcd * (DV / 16);
-  // Each scan wave streams its whole record through its CU's vector memory
-  // path, which one wave nearly saturates.  When there are no more waves
-  // than CUs, reserve enough LDS (unused) that no two of them share a CU.
-  int lds_pad = 0;
-  if (blocks <= kNumCU) {
-    lds_pad = kSpreadLds;
-    hipError_t e = hipFuncSetAttribute((const void*)ks, hipFuncAttributeMaxDynamicSharedMemorySize, lds_pad);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(ks, dim3((unsigned)blocks), dim3(256), lds_pad, st,
+  hipLaunchKernelGGL(ks, dim3((unsigned)blocks), dim3(256), 0, st,
                      static_cast<const TIn*>(a.v), static_cast<TIn*>(a.o), a.cu_seqlens, a.n_seqs,
-                     a.total_tokens, a.H, cap, off, recs, static_cast<TPool*>(a.pool.base),
+                     a.total_tokens, a.H, w.cap, w.off, w.recs, static_cast<TPool*>(a.pool.base),
                      a.pool.n_slots, a.init_slot, a.final_slot, a.track_ptr, a.track_chunk,
                      a.track_slot, a.n_track, a.track_f32, a.dev_err);
   return hipGetLastError();
@@ -1202,15 +751,15 @@ size_t prefill_workspace_bytes(int n_seqs, int64_t total_tokens, int H, int dk, 
   (void)dv;
   (void)in_dtype;
   int64_t rec = 0;
-  if (dk == 128 && chunk == 64) rec = Rec<128, 64, bf16>::kBytes;
+  if (dk == 128 && chunk == 64) rec = rec16_bytes();
   else if (dk == 16 && chunk == 16) rec = Rec<16, 16, float>::kBytes;
   return (size_t)(map_bytes(n_seqs) + chunk_upper_bound(total_tokens, n_seqs, chunk) * H * rec);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
-  if (a.dk == 128 && a.dv == 128 && a.chunk == 64) {
-    if (a.in_dtype == BF16) return by_pool<128, 128, 64, bf16, bf16>(a, st);
-    if (a.in_dtype == F16) return by_pool<128, 128, 64, f16, f16>(a, st);
+  if (a.dk == 128 && a.dv == 128 && a.chunk == 64 && (a.in_dtype == BF16 || a.in_dtype == F16)) {
+    const WsView w = map_chunks(a, st, 64);
+    return launch_prefill16(a, st, w.cap, w.off, w.recs);
   }
   if (a.dk == 16 && a.dv == 16 && a.chunk == 16 && a.in_dtype == F32)
     return by_pool<16, 16, 16, float, float>(a, st);

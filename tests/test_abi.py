@@ -90,7 +90,7 @@ def test_prefill_host_errors(L):
 def test_workspace_query(L):
     out = ctypes.c_size_t(0)
     assert L.kda_chunk_prefill_workspace(16, 135168, 32, 128, 128, 64, 2, ctypes.byref(out)) == 0
-    rec = 66304                               # bytes per (chunk, head) record at d=128, C=64, bf16
+    rec = 55808                               # bytes per (chunk, head) record at d=128, C=64, bf16
     assert out.value == 256 + (135168 // 64 + 16) * 32 * rec
     assert kda.prefill_workspace_bytes(1, 64, 2, 16, 16, 16, __import__("torch").float32) > 0
     assert L.kda_chunk_prefill_workspace(1, 64, 2, 32, 32, 16, 2, ctypes.byref(out)) == 2
