@@ -218,7 +218,7 @@ def main():
     dominant = max(calls, key=lambda c: ms[c])
     if dominant == "prefill":
         achieved = p_bytes / p_s / 1e9
-        roof = {"kernel": "kda_chunk_prefill (kda_chunk_map + kda_chunk_prep + kda_chunk_scan)",
+        roof = {"kernel": "kda_chunk_prefill (kda_chunk_map + kda_chunk_prep16 + kda_chunk_scan16)",
                 "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                 "frac": achieved * 1e9 / HBM_PEAK, "traffic": measured_prefill_traffic(),
                 "algorithmic_bytes_per_launch": p_bytes, "avg_launch_ms": ms["prefill"]}
