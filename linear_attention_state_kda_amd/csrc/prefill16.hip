@@ -111,7 +111,7 @@ __device__ __forceinline__ void put_half(void* slot, int hf, floatx4 x) {
   *reinterpret_cast<typename Vec4<T>::type*>(static_cast<uint8_t*>(slot) + 8 * hf) = cvt4<T>(x);
 }
 
-// LDS of the prep, 38.25 KiB: regions reused across phases (the comments
+// LDS of the prep, 39.25 KiB: regions reused across phases (the comments
 // give the phases that hold each view).
 struct Prep16Smem {
   union {
@@ -123,6 +123,7 @@ struct Prep16Smem {
     } t;
   } r1;
   union {
+    uint4 stage[4][16][17];    // input rows [wave][row][16-byte piece], padded       (inputs)
     uint4 kbt[8][2][64];       // Kb^T fragments [key tile][token block][lane]        (Kb^T, Z)
   } r2;
   union {
@@ -168,28 +169,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   const int n = min(C, len - c * C);
   uint8_t* rec = recs + ((int64_t)h * cap + j) * R::kBytes;
 
-  // ---- inputs of this lane's token; rows past the chunk's end lie outside
-  //      the buffer range and read as zero (zero keys, queries and gates)
+  // ---- inputs.  Each wave loads its 16 token rows of k, q, g as whole rows
+  //      (16 bytes per lane, 1 KiB per load: one L1 request per line), then
+  //      regroups them through its own rows of LDS into the fragment layout.
+  //      Rows past the chunk's end lie outside the buffer range and read as
+  //      zero (zero keys, queries and gates).
   const int t = 16 * w + r;
   const bool valid = t < n;
   const int64_t hd = (int64_t)H * DK;
+  const int64_t row = (int64_t)(t0 + min(t, n - 1));
+  const T braw = bl[row * H + h];
   const int64_t cbase = (int64_t)t0 * hd + (int64_t)h * DK;
   const uint32_t nbytes = (uint32_t)(((int64_t)(n - 1) * hd + DK) * (int64_t)sizeof(T));
   const auto rk = buffer_rsrc(k + cbase, nbytes), rq = buffer_rsrc(q + cbase, nbytes),
              rg = buffer_rsrc(g + cbase, nbytes);
-  const int voff = (int)(((int64_t)t * hd + 4 * gq) * (int64_t)sizeof(T));
+  uint4 graw[4], kraw[4], qraw[4];
+#pragma unroll
+  for (int jr = 0; jr < 4; ++jr) {  // rows 16w + 4jr + (lane / 16), bytes 16 (lane % 16) ..
+    const int voff = (int)((int64_t)(16 * w + 4 * jr + (lane >> 4)) * hd * (int64_t)sizeof(T)) + 16 * r;
+    graw[jr] = ld16(rg, voff, 0);
+    kraw[jr] = ld16(rk, voff, 0);
+    qraw[jr] = ld16(rq, voff, 0);
+  }
   In4 kr[NFK][2], qr[NFK][2], grw[NFK][2];
+  auto regroup = [&](const uint4 (&raw)[4], In4 (&out)[NFK][2]) {
 #pragma unroll
-  for (int kb = 0; kb < NFK; ++kb)
+    for (int jr = 0; jr < 4; ++jr) sm.r2.stage[w][4 * jr + (lane >> 4)][r] = raw[jr];
+    wave_sync();
+    const uint8_t* rowp = reinterpret_cast<const uint8_t*>(&sm.r2.stage[w][r][0]);
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int so = (32 * kb + 16 * hf) * (int)sizeof(T);
-      kr[kb][hf] = __builtin_bit_cast(In4, __builtin_amdgcn_raw_buffer_load_b64(rk, voff, so, 0));
-      qr[kb][hf] = __builtin_bit_cast(In4, __builtin_amdgcn_raw_buffer_load_b64(rq, voff, so, 0));
-      grw[kb][hf] = __builtin_bit_cast(In4, __builtin_amdgcn_raw_buffer_load_b64(rg, voff, so, 0));
-    }
-  const int64_t row = (int64_t)(t0 + min(t, n - 1));
-  const float beta = valid ? sigmoidf_(to_f32(bl[row * H + h])) : 0.f;
+    for (int kb = 0; kb < NFK; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        out[kb][hf] = *reinterpret_cast<const In4*>(rowp + 64 * kb + 32 * hf + 8 * gq);
+    wave_sync();
+  };
+  regroup(graw, grw);
+  regroup(kraw, kr);
+  regroup(qraw, qr);
+  const float beta = valid ? sigmoidf_(to_f32(braw)) : 0.f;
   if (gq == 0) sm.beta[t] = beta;
 
   // ---- Gamma: prefix sums of g over the tile's 16 tokens (DPP), then the
