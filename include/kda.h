@@ -139,13 +139,16 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
                              void* stream);
 
 /* Speculative-decode verify ([P3] step 3): per request, read the checkpoint
- * in pool slot ckpt_slot[r] (never written), step the L positions token by
- * token with the gate activations applied inside the kernel, and write
+ * in pool slot ckpt_slot[r] (never written), run the token recurrence over
+ * the L positions with the gate activations applied inside the kernel, and
+ * write
  *   o       [n_req][L][H][d_v] in in_dtype,
  *   u_rec   [n_req][H][L][d_v] fp32 correction u_t (beta folded in),
  *   kg_rec  [n_req][H][L][2*d_k] in in_dtype: key k_t then raw gate g_t.
  * 1 <= L <= 256.  q, k, v, g, o, u_rec and kg_rec must be 16-byte aligned
- * (KDA_ERR_INVALID_ARG otherwise). */
+ * (KDA_ERR_INVALID_ARG otherwise).  A request whose ckpt_slot is outside
+ * [0, n_slots) sets KDA_DEV_ERR_SLOT in *dev_err and its outputs are left
+ * unwritten; the other requests are computed as usual. */
 kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, const void* g,
                                 const void* b, int32_t in_dtype, void* o, int32_t n_req,
                                 int32_t L, int32_t H, int32_t d_k, int32_t d_v, kda_pool pool,

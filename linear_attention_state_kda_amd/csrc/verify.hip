@@ -1,26 +1,36 @@
 // RecoverSSM verify for gfx950 (vLLM PR #51855 summary, implementation
 // breakdown step 3): read one checkpoint per request (never written), step the
-// L speculative positions token by token, and record per position the fp32
-// correction u_t plus a lossless copy of the key and raw gate.  The gate
-// activations (alpha = exp(g), beta = sigmoid(b)) are applied inside the
-// kernel, with the same fp32 code as the prefill path.
+// L speculative positions, and record per position the fp32 correction u_t
+// plus a lossless copy of the key and raw gate.  The gate activations
+// (alpha = exp(g), beta = sigmoid(b)) are applied inside the kernel, with the
+// same fp32 code as the prefill path.
 //
-// One workgroup (4 waves) per (request, head); the d x d fp32 state stays in
-// registers.  An 8-lane group owns 4 state rows (v) and each lane 16 of their
-// 128 key entries, k in {4*(lane%8) + 32*j + e}, so each checkpoint load is
-// a contiguous 128 bytes per group.  Within a block of kTB positions the
-// state is held as S = Diag(D) St, D_t[k] being the product of alpha[k] over
-// the block's positions up to and including t.  Then, per position t:
-//   S_dec^T k = St^T (D_t k),  S_dec^T q = St^T (D_t q)     (S_dec = Diag(alpha_t) S)
-//   u = beta (v - S_dec^T k),  o = S_dec^T q + u (k . q)
-//   St += (k / D_t) u^T                                      (one FMA per element)
-// and at the end of a block St <- Diag(D) St restarts D at 1.  The two dot
-// products reduce across the 8 lanes of a group with DPP, so every lane gets
-// its own rows' u with no LDS traffic per position.  The per-position vectors
-// (D_t k, D_t q, k / D_t, v, beta, k . q) of a block are built once behind one
-// barrier.  D and 1/D stay finite in fp32 while the summed gate over a block
-// stays above about -80 (the chunked path's bound over a whole chunk is the
-// same, so verify is the less restrictive of the two).
+// Two workgroups (4 waves each) per (request, head), one per half of the
+// state's value columns: every step below is independent across value
+// columns except the per-position vectors and two 8 x 8 matrices, which both
+// halves form from the same key/gate/query rows.  The d x (d/2) fp32 state
+// half stays in registers as MFMA accumulator tiles.  The workgroups are
+// persistent (a few per compute unit, each stepping through many items).
+//
+// Positions go in blocks of kTB = 8.  Within a block the state is held as
+// S = Diag(D) St, D_t[k] being the product of alpha[k] over the block's
+// positions up to and including t; with wk_t = D_t k_t, wq_t = D_t q_t,
+// ku_t = k_t / D_t and S_dec,t = Diag(alpha_t) S_{t-1}:
+//   S_dec,t^T k_t = St_0^T wk_t + sum_{s<t} u_s (ku_s . wk_t)
+//   S_dec,t^T q_t = St_0^T wq_t + sum_{s<t} u_s (ku_s . wq_t)
+//   u_t = beta_t (v_t - S_dec,t^T k_t),   o_t = S_dec,t^T q_t + u_t (k_t . q_t)
+// so that, column by column of the state, with the Gram matrix
+// G[s][n] = ku_s . [wk | wq]_n (n < 8: wk, n >= 8: wq):
+//   u = T Diag(beta) (v - St_0^T wk),  T = (I + Diag(beta) Lk)^-1,
+//       Lk[t][s] = G[s][t] for s < t  (the token recursion solved per block)
+//   o = St_0^T wq + P u,  P[t][s] = G[s][8 + t] for s <= t  (ku_t . wq_t = k_t . q_t)
+//   St_0 <- Diag(D_block) (St_0 + sum_t ku_t u_t^T)  (multi-block windows)
+// Per block that is one fp32 MFMA product with the state, St_0^T [wk | wq],
+// two products of its result with the 8 x 8 matrices T Diag(beta) and
+// [P | I] (shared by all value columns), and the rank-8 update.  D and 1/D stay finite
+// in fp32 while the summed gate over a block stays above about -80.
+#include <algorithm>
+
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
@@ -30,18 +40,38 @@ namespace {
 
 constexpr int kT = 256;
 constexpr int kD = 128;   // state rows (d_v) and columns (d_k)
-constexpr int kTB = 8;    // positions prepared per block
+constexpr int kDH = 64;   // value columns per workgroup
+constexpr int kTB = 8;    // positions per block
+constexpr int kWS = kD + 4;   // padded row stride (floats) of the per-position vectors
+constexpr int kXcd = 8;   // consecutive workgroup ids go to the 8 XCDs in turn
 
-// Sum over the 8 lanes of a group, result in every lane of the group.
-__device__ __forceinline__ float group8_sum(float x) {
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));  // lane ^ 1
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));  // lane ^ 2
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, true)); // 7 - lane in 8
-  return x;
+// Workgroups per compute unit: the register budget allows 4 for one-block
+// windows with 16-bit rows, 3 otherwise.
+constexpr int resident_wgs(size_t in_bytes, bool multi) { return multi ? 2 : in_bytes == 2 ? 4 : 3; }
+
+// fp32 16x16x4 MFMA.  A: lane l holds A[l % 16][l / 16]; B: lane l holds
+// B[l / 16][l % 16]; C/D: lane l holds D[4 (l / 16) + i][l % 16].
+__device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <typename TIn, typename TPool>
-__global__ __launch_bounds__(kT) void kda_verify_kernel(
+// Copy N bytes (4, 8 or 16; both addresses N-aligned) with one vector store.
+template <int N, typename TD, typename TS>
+__device__ __forceinline__ void store_n(TD* dst, const TS* src) {
+  typedef unsigned int vec __attribute__((ext_vector_type(N / 4)));
+  *reinterpret_cast<vec*>(dst) = *reinterpret_cast<const vec*>(src);
+}
+
+// LDS writes of this wave visible to its other lanes
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// kMulti: windows longer than one block (the state is updated between blocks)
+template <typename TIn, typename TPool, bool kMulti>
+__global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(resident_wgs(sizeof(TIn), kMulti), 8))) void kda_verify_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const TIn* __restrict__ g, const TIn* __restrict__ bl, TIn* __restrict__ o, int n_req, int L,
     int H, const TPool* __restrict__ pool, int64_t n_slots, const int32_t* __restrict__ ckpt,
@@ -49,160 +79,304 @@ __global__ __launch_bounds__(kT) void kda_verify_kernel(
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   constexpr int EP = 16 / (int)sizeof(TIn);   // input elements per 16-byte piece
   constexpr int PPR = kD / EP;                 // pieces per 128-element row
-  // per position of the block: D_t k, D_t q (for the dots), k / D_t (update)
-  __shared__ __align__(16) float s_wk[kTB][kD];
-  __shared__ __align__(16) float s_wq[kTB][kD];
-  __shared__ __align__(16) float s_ku[kTB][kD];
-  __shared__ __align__(16) float s_dec[kD];      // D at the end of the block
-  __shared__ float s_beta[kTB], s_kq[2][kTB];    // k . q as two 64-channel halves
-  // the block's inputs as loaded (rows of 128: k, g, q, v), and its outputs
-  // u and o, so that every global access moves 16 bytes per lane
-  __shared__ __align__(16) TIn s_in[4][kTB][kD];
-  __shared__ __align__(16) float s_u[kTB][kD];
-  __shared__ __align__(16) TIn s_o[kTB][kD];
+  constexpr int NKGQ = 3 * kTB * PPR;          // pieces of the k, g, q rows
+  constexpr int NP = NKGQ + kTB * PPR / 2;     // ... and of this half of the v rows
+  constexpr int NR = (NP + kT - 1) / kT;
+  // per block: [wk_t | wq_t] by row n (n < 8: wk, n >= 8: wq) and ku_t, rows
+  // padded so that 16 lanes reading 16 rows fall in different banks; the
+  // Gram matrix as four per-wave partial sums over 32 keys each; T Diag(beta)
+  // and [P | I] (rows t, 16 columns s; rows 8..15 and the identity block stay
+  // as set at the start); D at the block end; beta (zero past the block end)
+  __shared__ __align__(16) float s_w[2 * kTB][kWS];
+  __shared__ __align__(16) float s_ku[kTB][kWS];
+  __shared__ __align__(16) float s_gp[4][kTB][2 * kTB];
+  __shared__ __align__(16) float s_g[kTB][2 * kTB];
+  __shared__ __align__(16) float s_tb[16][20];
+  __shared__ __align__(16) float s_pi[16][20];
+  __shared__ __align__(16) float s_dec[kD];
+  __shared__ float s_beta[kTB];
+  // the block's inputs as loaded: rows of k, g, q ([3][kTB][kD]) then this
+  // half of the v rows ([kTB][kDH]), piece p of 16 bytes at byte 16 p; and
+  // the block's outputs u and o, so that every global access moves 16 bytes
+  // per lane
+  __shared__ __align__(16) TIn s_stage[NP * EP];
+  __shared__ __align__(16) float s_u[kTB][kDH];
+  __shared__ __align__(16) TIn s_o[kTB][kDH];
+  const TIn* const s_v = s_stage + NKGQ * EP;
+  auto s_in = [&](int a, int jj, int c) -> float { return to_f32(s_stage[(a * kTB + jj) * kD + c]); };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = lane >> 3, gl = lane & 7;       // 8 groups of 8 lanes
-  const int r = blockIdx.x / H, h = blockIdx.x % H;
-  if (r >= n_req) return;
-  const int slot = ckpt[r];
-  if (slot < 0 || (int64_t)slot >= n_slots) {
-    if (tid == 0 && h == 0) set_err(dev_err, 1u);
-    return;
+  const int gq = lane >> 4, r = lane & 15;
+  const int n_items = n_req * H;
+  const int64_t tok_stride = (int64_t)H * kD;
+
+  // Persistent: workgroups b and b + kXcd (same XCD) hold the two halves of
+  // one (request, head) and step through items together, gridDim.x / 2
+  // apart.  Items whose checkpoint slot is out of range are skipped (and
+  // flagged); their outputs are left untouched.
+  const int bid = blockIdx.x, vh = (bid / kXcd) & 1, stride = gridDim.x / 2;
+  auto first_valid = [&](int it) -> int {
+    for (; it < n_items; it += stride) {
+      const int s = ckpt[it / H];
+      if (s >= 0 && (int64_t)s < n_slots) break;
+      if (tid == 0 && vh == 0) set_err(dev_err, 1u);
+    }
+    return it;
+  };
+  int item = first_valid((bid / (2 * kXcd)) * kXcd + bid % kXcd);
+  if (item >= n_items) return;
+
+  for (int e = tid; e < 16 * 20; e += kT) {
+    const int t = e / 20, c = e % 20;
+    (&s_tb[0][0])[e] = 0.f;
+    (&s_pi[0][0])[e] = (t < kTB && c == kTB + t) ? 1.f : 0.f;
   }
 
-  // ---- checkpoint: rows row0 + i (i < 4), keys 4*gl + 32*j + e
-  const int row0 = 32 * wave + 4 * grp;
-  floatx4 S[4][4];
-  const TPool* src = pool + ((int64_t)slot * H + h) * kD * kD;
+  // the input rows of block t0 of an item (rows past the block end repeat
+  // its last position; pieces past the end reload the last one), and this
+  // half of an item's checkpoint as MFMA tiles: wave w owns value columns
+  // 64 vh + 16 w + r, and tile kt of lane (g, r) holds St[16 kt + 4g + e][that
+  // column], four consecutive keys of one pool row (pool layout [v][k])
+  u32x4 buf[NR];
+  TIn braw;   // converted where used, so that no wait follows the load
+  auto load_rows = [&](int it, int t0) {
+    const int rq = it / H, h = it % H, nb = min(kTB, L - t0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int pp = 0; pp < NR; ++pp) {
+      const int pc = min(tid + kT * pp, NP - 1);
+      const bool is_v = pc >= NKGQ;
+      const int a = pc / (kTB * PPR);
+      const int jj = is_v ? (pc - NKGQ) / (PPR / 2) : (pc / PPR) % kTB;
+      const int col = is_v ? vh * kDH + ((pc - NKGQ) % (PPR / 2)) * EP : (pc % PPR) * EP;
+      const TIn* const base = a == 0 ? k : a == 1 ? g : a == 2 ? q : v;
+      buf[pp] = *reinterpret_cast<const u32x4*>(
+          base + ((int64_t)rq * L + t0 + min(jj, nb - 1)) * tok_stride + (int64_t)h * kD + col);
+    }
+    braw = bl[((int64_t)rq * L + t0 + min(tid & (kTB - 1), nb - 1)) * H + h];
+  };
+  floatx4 S[8];
+  auto load_state = [&](int it) {
+    const TPool* const src =
+        pool + ((int64_t)ckpt[it / H] * H + it % H) * kD * kD + (int64_t)vh * kDH * kD;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) S[i][j] = load4(src + (row0 + i) * kD + 4 * gl + 32 * j);
-
-  const int64_t tok_stride = (int64_t)H * kD;
-  const TIn* const arr[4] = {k, g, q, v};
-  TIn* const kg_rh = kg_rec + ((int64_t)r * H + h) * L * (2 * kD);   // [L][2 kD] of this (req, head)
-  float* const u_rh = u_rec + ((int64_t)r * H + h) * L * kD;        // [L][kD]
-  for (int t0 = 0; t0 < L; t0 += kTB) {
-    const int nb = min(kTB, L - t0);
-    if (t0 > 0) __syncthreads();  // every wave is done with the previous block
-    // ---- stage the block's rows: piece p = (array, position, part); rows
-    //      past the block end repeat its last position
+    for (int kt = 0; kt < 8; ++kt) S[kt] = load4(src + (16 * wave + r) * kD + 16 * kt + 4 * gq);
+  };
+  int t0 = 0, rq = 0, h = 0, nb = 0;
+  bool last = true;   // the item's last block (always, for one-block windows)
+  floatx4 dot;        // St_0^T [wk | wq] of the current block
+  auto head = [&]() {
+    rq = item / H;
+    h = item % H;
+    nb = min(kTB, L - t0);
 #pragma unroll
-    for (int pp = 0; pp < 4 * kTB * PPR / kT; ++pp) {
+    for (int pp = 0; pp < NR; ++pp) {
       const int pc = tid + kT * pp;
-      const int a = pc / (kTB * PPR), jj = (pc / PPR) % kTB, part = pc % PPR;
-      const int64_t off = ((int64_t)r * L + t0 + min(jj, nb - 1)) * tok_stride + (int64_t)h * kD + part * EP;
-      *reinterpret_cast<u32x4*>(&s_in[a][jj][part * EP]) = *reinterpret_cast<const u32x4*>(arr[a] + off);
+      if (pc < NP) *reinterpret_cast<u32x4*>(&s_stage[pc * EP]) = buf[pp];
     }
-    if (tid < kTB) s_beta[tid] = sigmoidf_(to_f32(bl[((int64_t)r * L + t0 + min(tid, nb - 1)) * H + h]));
+    if (tid < kTB) s_beta[tid] = tid < nb ? sigmoidf_(to_f32(braw)) : 0.f;
     __syncthreads();
-    // ---- records of k and the raw gate: [position][k | g], contiguous
+    // ---- per-position vectors: thread (key channel c, half hh) runs the
+    //      cumulative decay over positions 4 hh .. 4 hh + 3 (the second half
+    //      first runs it over positions 0..3); 1/D as a product of exp(-g)
+    {
+      const int c = tid & (kD - 1), hh = tid >> 7;
+      float D = 1.f, Di = 1.f;
+      if (hh) {
 #pragma unroll
-    for (int pp = 0; pp < 2 * kTB * PPR / kT; ++pp) {
-      const int pc = tid + kT * pp;
-      const int jj = pc / (2 * PPR), a = (pc / PPR) % 2, part = pc % PPR;
-      if (jj < nb)
-        *reinterpret_cast<u32x4*>(kg_rh + (int64_t)(t0 + jj) * (2 * kD) + a * kD + part * EP) =
-            *reinterpret_cast<const u32x4*>(&s_in[a][jj][part * EP]);
-    }
-    // ---- per-position vectors: threads 0..127 own one key channel each and
-    //      run the cumulative decay over the block
-    if (tid < kD) {
-      float D = 1.f;
-#pragma unroll
-      for (int jj = 0; jj < kTB; ++jj) {
-        const float kk = to_f32(s_in[0][jj][tid]), qq = to_f32(s_in[2][jj][tid]);
-        D *= __expf(to_f32(s_in[1][jj][tid]));
-        s_wk[jj][tid] = D * kk;
-        s_wq[jj][tid] = D * qq;
-        s_ku[jj][tid] = kk / D;
-        float p = kk * qq;
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) p += __shfl_xor(p, m);
-        if (lane == 0) s_kq[wave][jj] = p;
-      }
-      s_dec[tid] = D;  // read only when the block is full (a next block exists)
-    }
-    __syncthreads();
-
-    for (int jj = 0; jj < nb; ++jj) {
-      floatx4 wk[4], wq[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        wk[j] = *reinterpret_cast<const floatx4*>(&s_wk[jj][4 * gl + 32 * j]);
-        wq[j] = *reinterpret_cast<const floatx4*>(&s_wq[jj][4 * gl + 32 * j]);
-      }
-      float pred[4], oq[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float a = 0.f, b2 = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            a += S[i][j][e] * wk[j][e];
-            b2 += S[i][j][e] * wq[j][e];
-          }
-        pred[i] = group8_sum(a);
-        oq[i] = group8_sum(b2);
-      }
-      const float beta = s_beta[jj], kqv = s_kq[0][jj] + s_kq[1][jj];
-      float u[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) u[i] = beta * (to_f32(s_in[3][jj][row0 + i]) - pred[i]);
-      // lanes 0..3 of a group hold u and lanes 4..7 o, one row each
-      {
-        const int i = gl & 3;
-        const float ui = (i == 0) ? u[0] : (i == 1) ? u[1] : (i == 2) ? u[2] : u[3];
-        const float oqi = (i == 0) ? oq[0] : (i == 1) ? oq[1] : (i == 2) ? oq[2] : oq[3];
-        if (gl < 4) s_u[jj][row0 + i] = ui;
-        else s_o[jj][row0 + i] = from_f32<TIn>(oqi + ui * kqv);
-      }
-      if (t0 + jj + 1 < L) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const floatx4 ku = *reinterpret_cast<const floatx4*>(&s_ku[jj][4 * gl + 32 * j]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) S[i][j] += ku * u[i];
+        for (int jj = 0; jj < kTB / 2; ++jj) {
+          const float gg = s_in(1, jj, c);
+          D *= __expf(gg);
+          Di *= __expf(-gg);
         }
       }
+#pragma unroll
+      for (int j4 = 0; j4 < kTB / 2; ++j4) {
+        const int jj = (kTB / 2) * hh + j4;
+        const float kk = s_in(0, jj, c), qq = s_in(2, jj, c), gg = s_in(1, jj, c);
+        D *= __expf(gg);
+        Di *= __expf(-gg);
+        s_w[jj][c] = D * kk;
+        s_w[kTB + jj][c] = D * qq;
+        s_ku[jj][c] = kk * Di;
+      }
+      if (hh) s_dec[c] = D;  // read only when the block is full (a next block exists)
     }
-    // ---- rebase: St <- Diag(D_block) St, so the next block starts from D = 1
-    if (t0 + kTB < L) {
+    __syncthreads();
+    // ---- Gram partial of wave w over keys 32 w .. 32 w + 31: rows s (8 of
+    //      16 used), columns n; MFMA e of key group j contracts over keys
+    //      32 w + 16 j + 4g + e
+    {
+      floatx4 gp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const floatx4 d4 = *reinterpret_cast<const floatx4*>(&s_dec[4 * gl + 32 * j]);
+      for (int j = 0; j < 2; ++j) {
+        const int key = 32 * wave + 16 * j + 4 * gq;
+        const floatx4 ku4 = *reinterpret_cast<const floatx4*>(&s_ku[r & (kTB - 1)][key]);
+        const floatx4 a4 = r < kTB ? ku4 : floatx4{0.f, 0.f, 0.f, 0.f};
+        const floatx4 w4 = *reinterpret_cast<const floatx4*>(&s_w[r][key]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[i][j] = d4 * S[i][j];
+        for (int e = 0; e < 4; ++e) gp = mfma4(a4[e], w4[e], gp);   // A[s = r][key], B[key][n = r]
+      }
+      if (gq < 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_gp[wave][4 * gq + i][r] = gp[i];
       }
     }
     __syncthreads();
-    // ---- the block's u (fp32, contiguous per (req, head)) and o rows
+    // ---- one wave (a different one per item) sums the Gram partials and
+    //      forms T Diag(beta) and P; lane j < 8 solves column j of the unit
+    //      lower-triangular T by forward substitution
+    if (wave == (item & 3)) {
 #pragma unroll
-    for (int pp = 0; pp < kTB * kD / 4 / kT; ++pp) {
-      const int pc = tid + kT * pp;
-      const int jj = pc / (kD / 4), part = pc % (kD / 4);
-      if (jj < nb)
-        *reinterpret_cast<u32x4*>(u_rh + (int64_t)(t0 + jj) * kD + 4 * part) =
-            *reinterpret_cast<const u32x4*>(&s_u[jj][4 * part]);
+      for (int hf = 0; hf < 2; ++hf) {
+        const int e = lane + 64 * hf, s2 = e >> 4, n = e & 15;
+        const float gsum = s_gp[0][s2][n] + s_gp[1][s2][n] + s_gp[2][s2][n] + s_gp[3][s2][n];
+        if (n < kTB) s_g[s2][n] = gsum;
+        else s_pi[n - kTB][s2] = s2 <= n - kTB ? gsum : 0.f;
+      }
+      wave_sync();
+      if (lane < kTB) {
+        const int j = lane;
+        float tc[kTB];
+#pragma unroll
+        for (int t = 0; t < kTB; ++t) {
+          float acc = 0.f;
+#pragma unroll
+          for (int s2 = 0; s2 < t; ++s2) acc += s_g[s2][t] * tc[s2];
+          tc[t] = t == j ? 1.f : (t > j ? -s_beta[t] * acc : 0.f);
+        }
+        const float bj = s_beta[j];
+#pragma unroll
+        for (int t = 0; t < kTB; ++t) s_tb[t][j] = tc[t] * bj;
+      }
     }
-    for (int pc = tid; pc < kTB * PPR; pc += kT) {
-      const int jj = pc / PPR, part = pc % PPR;
-      if (jj < nb)
-        *reinterpret_cast<u32x4*>(o + ((int64_t)r * L + t0 + jj) * tok_stride + (int64_t)h * kD + part * EP) =
-            *reinterpret_cast<const u32x4*>(&s_o[jj][part * EP]);
+    // ---- St_0^T [wk | wq] as [n][v]: A = [wk | wq] rows n, B = the state
+    //      tile kt, whose accumulator element e is key 16 kt + 4g + e
+    dot = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) {
+      const floatx4 w4 = *reinterpret_cast<const floatx4*>(&s_w[r][16 * kt + 4 * gq]);  // A[n = r][key]
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dot = mfma4(w4[e], S[kt][e], dot);
+    }
+    // lane (g, r) now holds St_0^T wk_{4g+i} (g < 2) or St_0^T wq_{4g+i-8}
+    // (g >= 2) for value column 16 w + r
+  };
+  auto finish = [&]() {
+    TIn* const kg_rh = kg_rec + ((int64_t)rq * H + h) * L * (2 * kD);       // [L][2 kD] of this (req, head)
+    float* const u_rh = u_rec + ((int64_t)rq * H + h) * L * kD + vh * kDH;  // [L][kD], this half
+    __syncthreads();
+    const floatx4 tb4 = *reinterpret_cast<const floatx4*>(&s_tb[r][4 * gq]);
+    const floatx4 pi4 = *reinterpret_cast<const floatx4*>(&s_pi[r][4 * gq]);
+    floatx4 ua = {0.f, 0.f, 0.f, 0.f}, oa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float vv = to_f32(s_v[((4 * gq + i) & (kTB - 1)) * kDH + 16 * wave + r]);
+      ua = mfma4(tb4[i], gq < 2 ? vv - dot[i] : 0.f, ua);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) oa = mfma4(pi4[i], gq < 2 ? ua[i] : dot[i], oa);
+    if (gq < 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s_u[4 * gq + i][16 * wave + r] = ua[i];
+        s_o[4 * gq + i][16 * wave + r] = from_f32<TIn>(oa[i]);
+      }
+    }
+    // ---- St_0 += sum_t ku_t u_t^T (rank-8 MFMA update over this wave's
+    //      own columns), then the rebase St <- Diag(D_block) St so the
+    //      next block starts from D = 1
+    // the record rows are read here, before the barrier after which the
+    // next item's rows may overwrite the staging area
+    const int jk = min((kTB / 2) * vh + tid / 64, nb - 1), ek = (tid % 64) * 4;
+    typedef unsigned int kgvec __attribute__((ext_vector_type(sizeof(TIn))));
+    const kgvec kgv = *reinterpret_cast<const kgvec*>(&s_stage[((ek / kD) * kTB + jk) * kD + ek % kD]);
+    if (!last) {
+      wave_sync();
+#pragma unroll
+      for (int kt = 0; kt < 8; ++kt) {
+        const float a0 = s_ku[gq][16 * kt + r], a1 = s_ku[4 + gq][16 * kt + r];  // A[key = r][s = 4j + g]
+        S[kt] = mfma4(a0, s_u[gq][16 * wave + r], S[kt]);                        // B[s = 4j + g][v = r]
+        S[kt] = mfma4(a1, s_u[4 + gq][16 * wave + r], S[kt]);
+        const floatx4 d4 = *reinterpret_cast<const floatx4*>(&s_dec[16 * kt + 4 * gq]);
+        S[kt] = d4 * S[kt];
+      }
+    }
+    __syncthreads();
+    // ---- the block's outputs, one store per array per thread so that
+    //      every thread issues the same stores (the waits on the loads in
+    //      flight then never include them); rows past the block end
+    //      rewrite the last position with the same bytes.  Records of k
+    //      and the raw gate ([position][k | g], contiguous): half vh
+    //      writes positions 4 vh .. 4 vh + 3.  u (fp32, contiguous per
+    //      (req, head)) and o: this half's 64 columns.
+    *reinterpret_cast<kgvec*>(kg_rh + (int64_t)(t0 + jk) * (2 * kD) + ek) = kgv;
+    {
+      const int jj = min(tid / 32, nb - 1), c = (tid % 32) * 2;
+      store_n<8>(u_rh + (int64_t)(t0 + jj) * kD + c, &s_u[jj][c]);
+      store_n<2 * sizeof(TIn)>(o + ((int64_t)rq * L + t0 + jj) * tok_stride + (int64_t)h * kD + vh * kDH + c,
+                               &s_o[jj][c]);
+    }
+  };
+
+  // One-block windows request the next item's rows and checkpoint right
+  // after the state product (the state registers are free, as no update
+  // follows); they arrive while the item finishes.  Every path into the
+  // loop's head has those loads followed by the same three stores, so the
+  // waits on the loads count the stores as still in flight.  Longer windows
+  // request each block's rows at the top of their loop.
+  if (!kMulti) {
+    load_rows(item, 0);   // rows first: they are needed first
+    load_state(item);
+    head();
+    int nitem = first_valid(item + stride);
+    if (nitem < n_items) {
+      load_rows(nitem, 0);
+      load_state(nitem);
+      finish();
+      item = nitem;
+      while (true) {
+        head();
+        nitem = first_valid(item + stride);
+        if (nitem >= n_items) break;
+        load_rows(nitem, 0);
+        load_state(nitem);
+        finish();
+        item = nitem;
+      }
+    }
+    finish();
+  } else {
+    while (true) {
+      load_rows(item, t0);
+      if (t0 == 0) load_state(item);
+      head();
+      last = t0 + kTB >= L;
+      const int nitem = last ? first_valid(item + stride) : item, nt0 = last ? 0 : t0 + kTB;
+      finish();
+      if (nitem >= n_items) break;
+      item = nitem;
+      t0 = nt0;
     }
   }
 }
 
 template <typename TIn>
 hipError_t by_pool(const VerifyArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)((int64_t)a.n_req * a.H)), block(kT);
+  // two workgroups per (request, head), in groups of 2 kXcd ids; no more
+  // than fit on the compute units at once, each stepping through items
+  const int64_t items = (int64_t)a.n_req * a.H;
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
+    return hipErrorInvalidDevice;
+  const int64_t full = (items + kXcd - 1) / kXcd * 2 * kXcd;
+  const int resident = resident_wgs(sizeof(TIn), a.L > kTB);
+  const int64_t cap = std::max<int64_t>(2 * kXcd, (int64_t)n_cu * resident / (2 * kXcd) * (2 * kXcd));
+  const dim3 grid((unsigned)std::min(full, cap)), block(kT);
 #define KDA_VERIFY_LAUNCH(TP)                                                                      \
-  hipLaunchKernelGGL((kda_verify_kernel<TIn, TP>), grid, block, 0, st,                             \
+  hipLaunchKernelGGL((a.L > kTB ? kda_verify_kernel<TIn, TP, true> : kda_verify_kernel<TIn, TP, false>), \
+                     grid, block, 0, st,                                                           \
                      static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),                   \
                      static_cast<const TIn*>(a.v), static_cast<const TIn*>(a.g),                   \
                      static_cast<const TIn*>(a.b), static_cast<TIn*>(a.o), a.n_req, a.L, a.H,      \

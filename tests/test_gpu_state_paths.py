@@ -130,6 +130,55 @@ def test_verify_long_window():
         assert rel_per_head(r["u"][i], r["u_ref"][i], 0) < 1e-4
 
 
+@pytest.mark.parametrize("L", [1, 3, 9, 13])
+def test_verify_window_lengths(L):
+    """One-block and multi-block windows (ragged last block) with more
+    (request, head) items than workgroups resident at once, so every
+    workgroup steps through several items."""
+    n_req = 40
+    r = run_verify_case(n_req=n_req, L=L, H=32, in_dtype="bf16", pool_dtype="f32", seed=40 + L)
+    worst_o = max(rel_per_head(r["o"][i], r["o_ref"][i], 1) for i in range(n_req))
+    worst_u = max(rel_per_head(r["u"][i], r["u_ref"][i], 0) for i in range(n_req))
+    assert worst_o < 2e-2
+    assert worst_u < 1e-4
+    assert np.array_equal(wl.exact(r["kg"]), r["kg_ref"])
+
+
+@pytest.mark.parametrize("L", [8, 11])
+def test_verify_bad_slot_skips_request(L):
+    """A request whose checkpoint slot is out of range is flagged and its
+    outputs are left as they were; the other requests are unaffected."""
+    n_req, H, d, seed = 40, 32, 128, 51
+    toks = wl.token_inputs(n_req * L, H, d, d, "bf16", seed, shape_prefix=(n_req, L))
+    n_slots = n_req + 3
+    ckpt = wl.distinct_slots(n_req, n_slots, seed).copy()
+    pool = make_pool(n_slots, H, d, d, "f32")
+    host = fill_slots(pool, ckpt, "f32", seed)
+    bad = {7: -1, 23: n_slots}
+    ck_dev = ckpt.copy()
+    for i, s in bad.items():
+        ck_dev[i] = s
+    dev = {n: toks[n].to(DEV) for n in "qkvgb"}
+    o = torch.full((n_req, L, H, d), 7.0, dtype=torch.bfloat16, device=DEV)
+    u_rec = torch.full((n_req, H, L, d), 7.0, dtype=torch.float32, device=DEV)
+    kg_rec = torch.full((n_req, H, L, 2 * d), 7.0, dtype=torch.bfloat16, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kda.recurrent_verify(dev["q"], dev["k"], dev["v"], dev["g"], dev["b"], pool, i32(ck_dev),
+                         o=o, u_rec=u_rec, kg_rec=kg_rec, dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() & kda.DEV_ERR_SLOT
+    for i in bad:
+        assert bool((o[i] == 7.0).all()) and bool((u_rec[i] == 7.0).all()) and bool((kg_rec[i] == 7.0).all())
+    good = [i for i in range(n_req) if i not in bad]
+    ex = {n: wl.exact(toks[n])[good] for n in "qkvgb"}
+    S0 = np.stack([np.swapaxes(wl.exact(host[int(ckpt[i])]), -1, -2) for i in good])
+    o_ref, u_ref, kg_ref, _ = ko.verify_ref(ex["q"], ex["k"], ex["v"], ex["g"], ex["b"], S0)
+    o_got, u_got = wl.exact(o.cpu())[good], u_rec.cpu().double().numpy()[good]
+    assert max(rel_per_head(o_got[j], o_ref[j], 1) for j in range(len(good))) < 2e-2
+    assert max(rel_per_head(u_got[j], u_ref[j], 0) for j in range(len(good))) < 1e-4
+    assert np.array_equal(wl.exact(kg_rec.cpu())[good], kg_ref)
+
+
 # ---------------------------------------------------------------- commit
 
 @pytest.mark.parametrize("pool_dtype,in_dtype", [("f32", "bf16"), ("bf16", "bf16"), ("f16", "bf16"),
