@@ -83,10 +83,22 @@ def spec_setup(dev):
     verify_bytes = n_req * H * (d * d * 4 + L * (4 * d * s_in + s_in + d * s_in + 4 * d + 2 * d * s_in))
     commit_bytes = sum(H * (2 * d * d * 4 + int(n) * (4 * d + 2 * d * s_in)) for n in acc if n > 0)
     copy_bytes = len(case["fork_src"]) * 2 * H * d * d * 4
+    # conv half of the state tuple: q, k, v short-conv windows of H*d channels,
+    # width 4 (3 history rows) plus L speculative rows, bf16, one slot per pool slot
+    conv_keep, conv_rows, conv_dim = 3, 3 + L, H * d
+    conv = [torch.zeros((case["n_slots"], conv_rows, conv_dim), dtype=torch.bfloat16, device=dev)
+            for _ in range(3)]
+    for c in conv:
+        c.normal_(generator=gen)
+    conv_op_bytes = 3 * conv_keep * conv_dim * 2 * 2          # read + write of the history rows
+    n_fork = len(case["fork_src"])
     return dict(case=case, t=t, pool=pool, o=o, u_rec=u_rec, kg_rec=kg_rec,
                 ckpt=i32(case["ckpt_slots"], dev), acc=i32(acc, dev),
                 src=i32(case["fork_src"], dev), dst=i32(case["fork_dst"], dev),
-                bytes=dict(verify=verify_bytes, commit=commit_bytes, copy=copy_bytes))
+                conv=conv, conv_keep=[conv_keep] * 3, zero_shift=i32([0] * n_fork, dev),
+                bytes=dict(verify=verify_bytes, commit=commit_bytes, copy=copy_bytes,
+                           conv_compact=conv_op_bytes * int((acc > 0).sum()),
+                           conv_fork=conv_op_bytes * n_fork))
 
 
 def measured_prefill_traffic():
@@ -156,7 +168,7 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    calls = ["prefill", "verify", "commit", "copy"]
+    calls = ["prefill", "verify", "commit", "conv_compact", "copy", "conv_fork"]
 
     def step(events=None):
         def mark(i):
@@ -171,13 +183,17 @@ def main():
         mark(2)
         kda.commit(sp["pool"], sp["ckpt"], sp["acc"], sp["u_rec"], sp["kg_rec"])
         mark(3)
-        kda.state_copy(sp["pool"], sp["src"], sp["dst"])
+        kda.conv_state_update(sp["conv"], sp["conv_keep"], sp["ckpt"], sp["ckpt"], sp["acc"])
         mark(4)
+        kda.state_copy(sp["pool"], sp["src"], sp["dst"])
+        mark(5)
+        kda.conv_state_update(sp["conv"], sp["conv_keep"], sp["dst"], sp["src"], sp["zero_shift"])
+        mark(6)
 
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[ev() for _ in range(5)] for _ in range(a.steps)]
+    evs = [[ev() for _ in range(len(calls) + 1)] for _ in range(a.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(a.steps):
@@ -194,7 +210,7 @@ def main():
     cold = None
     if a.cold_steps > 0:
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        cevs = [[ev() for _ in range(5)] for _ in range(a.cold_steps)]
+        cevs = [[ev() for _ in range(len(calls) + 1)] for _ in range(a.cold_steps)]
         for s in range(a.cold_steps):
             scratch.fill_(s & 0xFF)
             step(cevs[s])
@@ -214,7 +230,8 @@ def main():
 
     p_s = ms["prefill"] * 1e-3
     tokens_per_s = T / p_s
-    gbs = {c: sp["bytes"][c] / (ms[c] * 1e-3) / 1e9 for c in ("verify", "commit", "copy")}
+    state_calls = ("verify", "commit", "conv_compact", "copy", "conv_fork")
+    gbs = {c: sp["bytes"][c] / (ms[c] * 1e-3) / 1e9 for c in state_calls}
     dominant = max(calls, key=lambda c: ms[c])
     if dominant == "prefill":
         achieved = p_bytes / p_s / 1e9
@@ -233,14 +250,14 @@ def main():
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "single-layer KDA prefill T=8229 H=32 d_k=d_v=128 chunk=64 bf16 "
-                               "fp32-pool + spec-decode verify/commit/fork n_req=256 L=8 H=32",
+                               "fp32-pool + spec-decode verify/commit/fork n_req=256 L=8 H=32 "
+                               "+ conv-state compaction/fork (3 x 4096 channels, width 4, bf16)",
                    "global_batch": 1, "seq_len": T, "heads": 32, "head_dim": 128, "chunk": 64},
         "prefill": {"ms": ms["prefill"], "ms_spread": spread(per["prefill"]), "tokens_per_s": tokens_per_s,
                     "hbm_GBps": p_bytes / p_s / 1e9, "hbm_frac": p_bytes / p_s / HBM_PEAK,
                     "mfma_TFLOPs": p_flops / p_s / 1e12, "mfma_frac": p_flops / p_s / BF16_PEAK},
-        "verify": {"ms": ms["verify"], "ms_spread": spread(per["verify"]), "GBps": gbs["verify"], "hbm_frac": gbs["verify"] * 1e9 / HBM_PEAK},
-        "commit": {"ms": ms["commit"], "ms_spread": spread(per["commit"]), "GBps": gbs["commit"], "hbm_frac": gbs["commit"] * 1e9 / HBM_PEAK},
-        "copy": {"ms": ms["copy"], "ms_spread": spread(per["copy"]), "GBps": gbs["copy"], "hbm_frac": gbs["copy"] * 1e9 / HBM_PEAK},
+        **{c: {"ms": ms[c], "ms_spread": spread(per[c]), "GBps": gbs[c], "hbm_frac": gbs[c] * 1e9 / HBM_PEAK}
+           for c in state_calls},
         "roofline": roof,
         "cold": None if cold is None else {
             "note": "L2 and MALL flushed by a 512 MiB write before each step",

@@ -86,6 +86,7 @@ typedef enum { KDA_F32 = 0, KDA_F16 = 1, KDA_BF16 = 2 } kda_dtype;
 #define KDA_DEV_ERR_TRACK 2u  /* a snapshot chunk outside [0, floor(T_i / chunk)], or a bad track_ptr */
 #define KDA_DEV_ERR_ACCEPT 4u /* an accepted length outside [0, L] */
 #define KDA_DEV_ERR_SEQLEN 8u /* cu_seqlens decreasing, negative, or beyond total_tokens */
+#define KDA_DEV_ERR_SHIFT 16u /* a conv-state shift outside [0, rows - keep] */
 
 /* A slot-indexed state pool, passed by value.  base points to
  * n_slots * H * d_v * d_k elements of `dtype` (a kda_dtype value). */
@@ -174,6 +175,49 @@ kda_status kda_commit(kda_pool pool, const int32_t* ckpt_slot, const int32_t* ds
  * disjoint from the sources; src == dst is a no-op. */
 kda_status kda_state_copy(kda_pool pool, const int32_t* src_slot, const int32_t* dst_slot,
                           int32_t n_pairs, int32_t* dev_err, void* stream);
+
+/* One conv tensor (a short-convolution window of the state tuple) for
+ * kda_conv_state_update.  Slot s, row r, channel c is the element at byte
+ * base + s * slot_stride + (r * dim + c) * elem_bytes: per slot, `rows`
+ * positions of `dim` channels, position-major; the first `keep` rows are
+ * the history carried between steps (the convolution width minus one), the
+ * rest an extended window's speculative positions.  Requirements (checked
+ * on the host): base 16-byte aligned; slot_stride a multiple of 16 and at
+ * least rows * dim * elem_bytes; 1 <= keep <= rows; elem_bytes 2 or 4 and
+ * dim * elem_bytes a multiple of 16 (KDA_ERR_UNSUPPORTED otherwise). */
+#define KDA_MAX_CONV_TENSORS 8
+typedef struct {
+  void* base;
+  int64_t slot_stride;
+  int64_t n_slots;
+  int32_t rows;
+  int32_t keep;
+  int32_t dim;
+  int32_t elem_bytes;
+} kda_conv_tensor;
+
+/* Fused conv-state update ([P1] sec. 2: the conv-state slots of many
+ * tensors cleared or copied in one launch, the conv window moved by an
+ * offset copy; [P3] steps 2 and 4: the extended window kept under
+ * speculation and compacted to the accepted length at commit).
+ * tensors: host array of n_tensors (1..KDA_MAX_CONV_TENSORS) descriptors,
+ * read during the call only.  dst_slot, src_slot, shift: device arrays of
+ * n_ops.  Op i applies to every tensor:
+ *   src_slot[i] == -1: every row of slot dst_slot[i] becomes zero;
+ *   otherwise rows [0, keep) of dst_slot[i] become rows
+ *   [shift[i], shift[i] + keep) of src_slot[i]; rows >= keep of the
+ *   destination are left as they were.  shift 0 copies the history (fork);
+ *   src == dst with shift n compacts the window after n accepted positions.
+ * Bits are copied, never converted.  The ops run concurrently: destinations
+ * must be distinct, and no op may read a slot another op writes (an op may
+ * read its own destination).  An op with a slot outside [0, n_slots) of
+ * any tensor (or src < -1) sets KDA_DEV_ERR_SLOT, one with a shift outside
+ * [0, rows - keep] of any tensor sets KDA_DEV_ERR_SHIFT; either way the op
+ * is skipped for every tensor.  n_ops == 0 launches nothing. */
+kda_status kda_conv_state_update(const kda_conv_tensor* tensors, int32_t n_tensors,
+                                 const int32_t* dst_slot, const int32_t* src_slot,
+                                 const int32_t* shift, int32_t n_ops, int32_t* dev_err,
+                                 void* stream);
 
 /* Static, NUL-terminated name of a status code. */
 const char* kda_status_string(kda_status status);

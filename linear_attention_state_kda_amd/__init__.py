@@ -16,8 +16,8 @@ import torch
 
 __all__ = [
     "KdaError", "lib", "DTYPE_CODES", "DEV_ERR_SLOT", "DEV_ERR_TRACK", "DEV_ERR_ACCEPT",
-    "DEV_ERR_SEQLEN", "prefill_workspace_bytes", "chunk_prefill", "recurrent_verify",
-    "commit", "state_copy", "LIB_PATH",
+    "DEV_ERR_SEQLEN", "DEV_ERR_SHIFT", "prefill_workspace_bytes", "chunk_prefill", "recurrent_verify",
+    "commit", "state_copy", "conv_state_update", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED",
           3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_LAUNCH"}
-DEV_ERR_SLOT, DEV_ERR_TRACK, DEV_ERR_ACCEPT, DEV_ERR_SEQLEN = 1, 2, 4, 8
+DEV_ERR_SLOT, DEV_ERR_TRACK, DEV_ERR_ACCEPT, DEV_ERR_SEQLEN, DEV_ERR_SHIFT = 1, 2, 4, 8, 16
 
 
 class KdaError(RuntimeError):
@@ -37,6 +37,12 @@ class KdaError(RuntimeError):
 class KdaPool(ctypes.Structure):
     _fields_ = [("base", ctypes.c_void_p), ("n_slots", ctypes.c_int64), ("dtype", ctypes.c_int32),
                 ("H", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32)]
+
+
+class KdaConvTensor(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("slot_stride", ctypes.c_int64), ("n_slots", ctypes.c_int64),
+                ("rows", ctypes.c_int32), ("keep", ctypes.c_int32), ("dim", ctypes.c_int32),
+                ("elem_bytes", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -52,6 +58,7 @@ _SIGS = {
                              _P, _P, _P, _P, _P],
     "kda_commit": [KdaPool, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P],
     "kda_state_copy": [KdaPool, _P, _P, _I32, _P, _P],
+    "kda_conv_state_update": [ctypes.POINTER(KdaConvTensor), _I32, _P, _P, _P, _I32, _P, _P],
     "kda_status_string": [_I32],
 }
 
@@ -197,3 +204,30 @@ def state_copy(pool, src_slot, dst_slot, dev_err=None):
     st = lib().kda_state_copy(_pool(pool), _ptr(src_slot), _ptr(dst_slot), src_slot.numel(),
                               _ptr(dev_err), _stream())
     _check(st, "kda_state_copy")
+
+
+def conv_state_update(tensors, keep, dst_slot, src_slot, shift, dev_err=None):
+    """kda_conv_state_update on conv tensors, each [n_slots, rows, dim] with
+    rows and channels contiguous (the slot stride may be larger); ``keep``
+    gives each tensor's history rows.  Op i: src_slot[i] == -1 clears slot
+    dst_slot[i]; otherwise rows [0, keep) of dst_slot[i] <- rows
+    [shift[i], shift[i] + keep) of src_slot[i]."""
+    if len(tensors) != len(keep):
+        raise ValueError("one keep value per tensor")
+    descs = (KdaConvTensor * max(1, len(tensors)))()
+    for i, (t, kp) in enumerate(zip(tensors, keep)):
+        if not t.is_cuda or t.dim() != 3:
+            raise ValueError("conv tensors must be 3-d device tensors [n_slots, rows, dim]")
+        n_slots, rows, dim = t.shape
+        if t.stride(2) != 1 or t.stride(1) != dim:
+            raise ValueError("rows and channels of a conv tensor must be contiguous")
+        descs[i] = KdaConvTensor(t.data_ptr(), t.stride(0) * t.element_size(), n_slots, rows, int(kp), dim,
+                                 t.element_size())
+    for name, x in (("dst_slot", dst_slot), ("src_slot", src_slot), ("shift", shift), ("dev_err", dev_err)):
+        _dev(x, name, dtype=torch.int32)
+    n = dst_slot.numel()
+    if src_slot.numel() != n or shift.numel() != n:
+        raise ValueError("dst_slot, src_slot and shift differ in length")
+    st = lib().kda_conv_state_update(descs, len(tensors), _ptr(dst_slot), _ptr(src_slot), _ptr(shift), n,
+                                     _ptr(dev_err), _stream())
+    _check(st, "kda_conv_state_update")

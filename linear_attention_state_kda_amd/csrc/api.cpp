@@ -3,6 +3,7 @@
 // rejected here, before any device memory is touched (vLLM PR #51855 summary,
 // risks item 1: a configuration the kernel cannot serve must fail at call
 // time, not inside the first step that hits it).
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include "../../include/kda.h"
@@ -147,6 +148,43 @@ kda_status kda_state_copy(kda_pool pool, const int32_t* src_slot, const int32_t*
   if (bpp * n_pairs > INT32_MAX) return KDA_ERR_UNSUPPORTED;
   kda::CopyArgs a{pool_desc(pool), src_slot, dst_slot, n_pairs, slot_bytes, dev_err};
   return launched(kda::launch_copy(a, static_cast<hipStream_t>(stream)));
+}
+
+static_assert(KDA_MAX_CONV_TENSORS == kda::kMaxConvTensors, "conv tensor limit");
+
+kda_status kda_conv_state_update(const kda_conv_tensor* tensors, int32_t n_tensors,
+                                 const int32_t* dst_slot, const int32_t* src_slot,
+                                 const int32_t* shift, int32_t n_ops, int32_t* dev_err,
+                                 void* stream) {
+  if (n_ops < 0 || tensors == nullptr || n_tensors < 1 || n_tensors > KDA_MAX_CONV_TENSORS)
+    return KDA_ERR_INVALID_ARG;
+  kda::ConvArgs a{};
+  a.set.n = n_tensors;
+  a.set.min_slots = INT64_MAX;
+  a.set.max_shift = INT32_MAX;
+  for (int i = 0; i < n_tensors; ++i) {
+    const kda_conv_tensor& t = tensors[i];
+    if (t.base == nullptr || (reinterpret_cast<uintptr_t>(t.base) & 15u) != 0 || t.n_slots <= 0 ||
+        t.rows < 1 || t.keep < 1 || t.keep > t.rows || t.dim < 1)
+      return KDA_ERR_INVALID_ARG;
+    if (t.elem_bytes != 2 && t.elem_bytes != 4) return KDA_ERR_UNSUPPORTED;
+    const int64_t row_bytes = (int64_t)t.dim * t.elem_bytes;
+    if (row_bytes % 16 != 0 || row_bytes * t.rows > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    if (t.slot_stride % 16 != 0 || t.slot_stride < row_bytes * t.rows) return KDA_ERR_INVALID_ARG;
+    a.set.t[i] = kda::ConvDesc{static_cast<uint8_t*>(t.base), t.slot_stride, t.n_slots, t.rows, t.keep,
+                               t.dim, t.elem_bytes};
+    a.set.min_slots = std::min<int64_t>(a.set.min_slots, t.n_slots);
+    a.set.max_shift = std::min(a.set.max_shift, t.rows - t.keep);
+  }
+  if (n_ops == 0) return KDA_OK;
+  if (dst_slot == nullptr || src_slot == nullptr || shift == nullptr) return KDA_ERR_INVALID_ARG;
+  if ((int64_t)n_ops * n_tensors > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  a.dst_slot = dst_slot;
+  a.src_slot = src_slot;
+  a.shift = shift;
+  a.n_ops = n_ops;
+  a.dev_err = dev_err;
+  return launched(kda::launch_conv_update(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

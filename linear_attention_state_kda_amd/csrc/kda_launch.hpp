@@ -63,6 +63,28 @@ struct CopyArgs {
   int32_t* dev_err;
 };
 
+// One conv tensor of a fused conv-state update: per slot `rows` positions of
+// `dim` channels (position-major), the first `keep` rows the carried history.
+constexpr int kMaxConvTensors = 8;
+struct ConvDesc {
+  uint8_t* base;
+  int64_t slot_stride;   // bytes
+  int64_t n_slots;
+  int rows, keep, dim, elem_bytes;
+};
+struct ConvSet {
+  ConvDesc t[kMaxConvTensors];
+  int n;
+  int64_t min_slots;   // smallest n_slots over the tensors
+  int max_shift;       // smallest rows - keep over the tensors
+};
+struct ConvArgs {
+  ConvSet set;
+  const int32_t *dst_slot, *src_slot, *shift;
+  int n_ops;
+  int32_t* dev_err;
+};
+
 // Shape support and sizes.
 bool prefill_supported(int dk, int dv, int chunk, int in_dtype, int pool_dtype);
 size_t prefill_workspace_bytes(int n_seqs, int64_t total_tokens, int H, int dk, int dv,
@@ -72,5 +94,6 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
+hipError_t launch_conv_update(const ConvArgs& a, hipStream_t s);
 
 }  // namespace kda

@@ -130,6 +130,32 @@ def test_verify_commit_copy_host_errors(L):
     assert s(n=0) == 0
 
 
+def conv_tensor(base=FAKE, stride=11 * 4096 * 2, n_slots=8, rows=11, keep=3, dim=4096, eb=2):
+    return kda.KdaConvTensor(base.value if base is not None else None, stride, n_slots, rows, keep, dim, eb)
+
+
+def test_conv_state_update_host_errors(L):
+    def call(ts, n=3, dst=FAKE, src=FAKE, sh=FAKE, n_t=None):
+        arr = (kda.KdaConvTensor * max(1, len(ts)))(*ts)
+        return L.kda_conv_state_update(arr, len(ts) if n_t is None else n_t, dst, src, sh, n, None, None)
+    good = conv_tensor()
+    assert call([good], n=0) == 0                        # nothing to do, nothing launched
+    assert call([good, conv_tensor(eb=4, dim=64, stride=11 * 64 * 4)], n=0) == 0
+    assert call([good], n=-1) == 1
+    assert call([], n=0, n_t=0) == 1
+    assert call([good] * 9, n=0) == 1                    # more than KDA_MAX_CONV_TENSORS
+    assert call([conv_tensor(base=None)], n=0) == 1
+    assert call([conv_tensor(base=ctypes.c_void_p(FAKE.value + 8))], n=0) == 1
+    assert call([conv_tensor(keep=0)], n=0) == 1
+    assert call([conv_tensor(keep=12)], n=0) == 1
+    assert call([conv_tensor(stride=11 * 4096 * 2 - 16)], n=0) == 1   # slots would overlap
+    assert call([conv_tensor(stride=11 * 4096 * 2 + 8)], n=0) == 1    # stride not a multiple of 16
+    assert call([conv_tensor(eb=8)], n=0) == 2
+    assert call([conv_tensor(dim=4100, stride=11 * 4100 * 2 + 8)], n=0) == 2   # row not 16-byte units
+    assert call([good], dst=None) == 1
+    assert call([good], sh=None) == 1
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(kda, "_lib", None)
     monkeypatch.setattr(kda, "LIB_PATH", str(tmp_path / "missing.so"))
