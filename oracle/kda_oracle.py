@@ -270,6 +270,62 @@ def commit_ref(S0, k_rec, g_rec, u_rec, n):
     return decay[:, :, None] * S0 + acc
 
 
+ERR_SLOT, ERR_ACCEPT = 1, 4
+
+
+def commit_align_ref(slots, block_table, num_tokens, accepted, block_size, k_rec, g_rec, u_rec):
+    """Align-mode RecoverSSM commit ([P3] Implementation breakdown steps 4-5
+    and the review's block-size check; the reading is this build's, the
+    pages give the commit plan only in outline).
+
+    The state is kept per block of ``block_size`` tokens: the state after p
+    tokens lives in the slot of the block holding token p (1-based), that is
+    block_table[r][(p - 1) // block_size]; a block's slot ends up holding the
+    state at its last token.  For request r with p = num_tokens[r] >= 1 and
+    n = accepted[r] accepted positions (p' = p + n), with b0 the block of
+    token p and b1 the block of token p' (block_size > n, so b1 <= b0 + 1):
+      b1 == b0: S_{p'} -> slot of b0 (nothing for n = 0);
+      b1 == b0 + 1: the state after the last accepted token still in b0
+        (m of them, possibly 0) -> slot of b0 (nothing for m = 0), and
+        S_{p'} -> slot of b1.
+    Every state is rebuilt from the checkpoint slots[slot of b0] with
+    ``commit_ref``.  slots: dict slot -> (H, d_k, d_v) state; block_table:
+    (n_req, blocks) ints; k_rec, g_rec: (n_req, H, L, d_k); u_rec:
+    (n_req, H, L, d_v).  Returns (dict slot -> new state, error bits); a
+    request with n outside [0, L] (ERR_ACCEPT), or p < 1, a block beyond its
+    table row or a slot not in ``slots`` (ERR_SLOT) is skipped.
+    """
+    L = u_rec.shape[2]
+    writes, err = {}, 0
+    for r in range(len(num_tokens)):
+        p, n = int(num_tokens[r]), int(accepted[r])
+        if not 0 <= n <= L:
+            err |= ERR_ACCEPT
+            continue
+        if p < 1:
+            err |= ERR_SLOT
+            continue
+        b0 = (p - 1) // block_size
+        # the accepted tokens p+1 .. p+n and the block each one falls in
+        blocks = [(p + j - 1) // block_size for j in range(1, n + 1)]
+        b1 = blocks[-1] if blocks else b0
+        if b1 >= len(block_table[r]) or int(block_table[r][b0]) not in slots or int(block_table[r][b1]) not in slots:
+            err |= ERR_SLOT
+            continue
+        s0, s1 = int(block_table[r][b0]), int(block_table[r][b1])
+        S0 = slots[s0]
+        rec = (k_rec[r], g_rec[r], u_rec[r])
+        if b1 == b0:
+            if n > 0:
+                writes[s0] = commit_ref(S0, *rec, n)
+        else:
+            m = sum(1 for b in blocks if b == b0)   # accepted tokens that close block b0
+            if m > 0:
+                writes[s0] = commit_ref(S0, *rec, m)
+            writes[s1] = commit_ref(S0, *rec, n)
+    return writes, err
+
+
 def copy_ref(pool, src, dst):
     """Rollback / fork as whole-state copies ([P1] Sec. 2 and Sec. 3).
 
