@@ -92,11 +92,25 @@ def spec_setup(dev):
         c.normal_(generator=gen)
     conv_op_bytes = 3 * conv_keep * conv_dim * 2 * 2          # read + write of the history rows
     n_fork = len(case["fork_src"])
+    # align mode: states per block of 64 tokens; request r holds pos[r] ~ U{1..4096}
+    # tokens, its checkpoint is its block's slot, the next block's slot is a fresh one
+    bs = 64
+    pos = np.random.default_rng([case["seed"], 77]).integers(1, 4097, n_req)
+    nb = 4096 // bs + 1
+    table = np.full((n_req, nb), -1, dtype=np.int32)
+    b0, b1 = (pos - 1) // bs, (pos + acc - 1) // bs
+    table[np.arange(n_req), b0] = case["ckpt_slots"]
+    table[np.arange(n_req), b0 + 1] = case["fork_dst"][:n_req]
+    closes = (b1 > b0) & (b1 * bs - pos > 0)
+    align_bytes = int(sum(H * (d * d * 4 * (2 + int(c)) + int(n) * (4 * d + 2 * d * s_in))
+                          for n, c in zip(acc, closes) if n > 0))
     return dict(case=case, t=t, pool=pool, o=o, u_rec=u_rec, kg_rec=kg_rec,
                 ckpt=i32(case["ckpt_slots"], dev), acc=i32(acc, dev),
                 src=i32(case["fork_src"], dev), dst=i32(case["fork_dst"], dev),
                 conv=conv, conv_keep=[conv_keep] * 3, zero_shift=i32([0] * n_fork, dev),
+                align_table=torch.as_tensor(table, device=dev), align_pos=i32(pos, dev), align_bs=bs,
                 bytes=dict(verify=verify_bytes, commit=commit_bytes, copy=copy_bytes,
+                           commit_align=align_bytes,
                            conv_compact=conv_op_bytes * int((acc > 0).sum()),
                            conv_fork=conv_op_bytes * n_fork))
 
@@ -168,7 +182,7 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    calls = ["prefill", "verify", "commit", "conv_compact", "copy", "conv_fork"]
+    calls = ["prefill", "verify", "commit", "commit_align", "conv_compact", "copy", "conv_fork"]
 
     def step(events=None):
         def mark(i):
@@ -183,12 +197,15 @@ def main():
         mark(2)
         kda.commit(sp["pool"], sp["ckpt"], sp["acc"], sp["u_rec"], sp["kg_rec"])
         mark(3)
-        kda.conv_state_update(sp["conv"], sp["conv_keep"], sp["ckpt"], sp["ckpt"], sp["acc"])
+        kda.commit_align(sp["pool"], sp["align_table"], sp["align_pos"], sp["acc"], sp["align_bs"],
+                         sp["u_rec"], sp["kg_rec"])
         mark(4)
-        kda.state_copy(sp["pool"], sp["src"], sp["dst"])
+        kda.conv_state_update(sp["conv"], sp["conv_keep"], sp["ckpt"], sp["ckpt"], sp["acc"])
         mark(5)
-        kda.conv_state_update(sp["conv"], sp["conv_keep"], sp["dst"], sp["src"], sp["zero_shift"])
+        kda.state_copy(sp["pool"], sp["src"], sp["dst"])
         mark(6)
+        kda.conv_state_update(sp["conv"], sp["conv_keep"], sp["dst"], sp["src"], sp["zero_shift"])
+        mark(7)
 
     for _ in range(a.warmup):
         step()
@@ -230,7 +247,7 @@ def main():
 
     p_s = ms["prefill"] * 1e-3
     tokens_per_s = T / p_s
-    state_calls = ("verify", "commit", "conv_compact", "copy", "conv_fork")
+    state_calls = ("verify", "commit", "commit_align", "conv_compact", "copy", "conv_fork")
     gbs = {c: sp["bytes"][c] / (ms[c] * 1e-3) / 1e9 for c in state_calls}
     dominant = max(calls, key=lambda c: ms[c])
     if dominant == "prefill":
@@ -251,7 +268,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "single-layer KDA prefill T=8229 H=32 d_k=d_v=128 chunk=64 bf16 "
                                "fp32-pool + spec-decode verify/commit/fork n_req=256 L=8 H=32 "
-                               "+ conv-state compaction/fork (3 x 4096 channels, width 4, bf16)",
+                               "+ align-mode commit (64-token blocks) + conv-state compaction/fork "
+                               "(3 x 4096 channels, width 4, bf16)",
                    "global_batch": 1, "seq_len": T, "heads": 32, "head_dim": 128, "chunk": 64},
         "prefill": {"ms": ms["prefill"], "ms_spread": spread(per["prefill"]), "tokens_per_s": tokens_per_s,
                     "hbm_GBps": p_bytes / p_s / 1e9, "hbm_frac": p_bytes / p_s / HBM_PEAK,

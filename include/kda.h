@@ -169,6 +169,34 @@ kda_status kda_commit(kda_pool pool, const int32_t* ckpt_slot, const int32_t* ds
                       int32_t rec_dtype, int32_t n_req, int32_t L, int32_t H, int32_t d_k,
                       int32_t d_v, int32_t* dev_err, void* stream);
 
+/* Align-mode commit ([P3] steps 4-5: the commit plan finds the accepted
+ * length and the block boundary, the running block index moves on; the
+ * review's check that the block size exceeds the speculative window).  The
+ * state is kept per block of block_size tokens: the state after p tokens
+ * lives in the slot of the block holding token p (1-based),
+ * block_table[r * blocks_per_req + (p - 1) / block_size], and a block's slot
+ * ends up holding the state at its last token.  Request r holds
+ * p = num_tokens[r] >= 1 tokens; with n = accepted_len[r] (0..L) accepted
+ * positions, b0 = (p - 1) / block_size and b1 = (p + n - 1) / block_size:
+ *   b1 == b0: the state after p + n tokens -> slot of b0, in place (n = 0
+ *             touches nothing);
+ *   b1 == b0 + 1: the state after the m = b1 * block_size - p accepted
+ *             tokens that close block b0 -> slot of b0 (when m > 0), and the
+ *             state after p + n tokens -> slot of b1.
+ * Both are rebuilt, as in kda_commit, from the checkpoint in b0's slot and
+ * the records of a verify call (one RNE cast each).  The running block of
+ * the next step is b1.  block_size > L is required (KDA_ERR_INVALID_ARG
+ * otherwise), so a window closes at most one block.  A request with n
+ * outside [0, L] sets KDA_DEV_ERR_ACCEPT; one with p < 1, b1 beyond its
+ * table row or a slot outside [0, n_slots) sets KDA_DEV_ERR_SLOT; either is
+ * skipped.  The slots of different requests must be distinct.  block_table,
+ * num_tokens, accepted_len: device arrays. */
+kda_status kda_commit_align(kda_pool pool, const int32_t* block_table, int32_t blocks_per_req,
+                            const int32_t* num_tokens, const int32_t* accepted_len,
+                            int32_t block_size, const float* u_rec, const void* kg_rec,
+                            int32_t rec_dtype, int32_t n_req, int32_t L, int32_t H, int32_t d_k,
+                            int32_t d_v, int32_t* dev_err, void* stream);
+
 /* Rollback / fork ([P1] secs. 2-3; one launch for many slots as in the
  * fused slot copy of sec. 2): for every pair i, pool slot dst_slot[i]
  * receives the bits of slot src_slot[i].  Destinations must be distinct and

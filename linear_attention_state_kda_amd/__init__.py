@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "KdaError", "lib", "DTYPE_CODES", "DEV_ERR_SLOT", "DEV_ERR_TRACK", "DEV_ERR_ACCEPT",
     "DEV_ERR_SEQLEN", "DEV_ERR_SHIFT", "prefill_workspace_bytes", "chunk_prefill", "recurrent_verify",
-    "commit", "state_copy", "conv_state_update", "LIB_PATH",
+    "commit", "commit_align", "state_copy", "conv_state_update", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -57,6 +57,8 @@ _SIGS = {
     "kda_recurrent_verify": [_P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, KdaPool,
                              _P, _P, _P, _P, _P],
     "kda_commit": [KdaPool, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P],
+    "kda_commit_align": [KdaPool, _P, _I32, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                         _P, _P],
     "kda_state_copy": [KdaPool, _P, _P, _I32, _P, _P],
     "kda_conv_state_update": [ctypes.POINTER(KdaConvTensor), _I32, _P, _P, _P, _I32, _P, _P],
     "kda_status_string": [_I32],
@@ -192,6 +194,23 @@ def commit(pool, ckpt_slot, accepted_len, u_rec, kg_rec, dst_slot=None, dev_err=
                           _ptr(u_rec), _ptr(kg_rec), DTYPE_CODES[kg_rec.dtype], n_req, L, H, dk,
                           dv, _ptr(dev_err), _stream())
     _check(st, "kda_commit")
+
+
+def commit_align(pool, block_table, num_tokens, accepted_len, block_size, u_rec, kg_rec, dev_err=None):
+    """kda_commit_align: block-aligned commit; block_table is [n_req, blocks_per_req] int32."""
+    n_req, H, L, dv = u_rec.shape
+    dk = kg_rec.shape[3] // 2
+    _dev(block_table, "block_table", dtype=torch.int32, ndim=2)
+    for name, t in (("num_tokens", num_tokens), ("accepted_len", accepted_len), ("dev_err", dev_err)):
+        _dev(t, name, dtype=torch.int32)
+    _dev(u_rec, "u_rec", dtype=torch.float32)
+    _dev(kg_rec, "kg_rec")
+    if block_table.shape[0] != n_req:
+        raise ValueError("block_table needs one row per request")
+    st = lib().kda_commit_align(_pool(pool), _ptr(block_table), block_table.shape[1], _ptr(num_tokens),
+                                _ptr(accepted_len), int(block_size), _ptr(u_rec), _ptr(kg_rec),
+                                DTYPE_CODES[kg_rec.dtype], n_req, L, H, dk, dv, _ptr(dev_err), _stream())
+    _check(st, "kda_commit_align")
 
 
 def state_copy(pool, src_slot, dst_slot, dev_err=None):

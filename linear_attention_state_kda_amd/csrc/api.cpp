@@ -133,6 +133,28 @@ kda_status kda_commit(kda_pool pool, const int32_t* ckpt_slot, const int32_t* ds
   return launched(kda::launch_commit(a, static_cast<hipStream_t>(stream)));
 }
 
+kda_status kda_commit_align(kda_pool pool, const int32_t* block_table, int32_t blocks_per_req,
+                            const int32_t* num_tokens, const int32_t* accepted_len,
+                            int32_t block_size, const float* u_rec, const void* kg_rec,
+                            int32_t rec_dtype, int32_t n_req, int32_t L, int32_t H, int32_t d_k,
+                            int32_t d_v, int32_t* dev_err, void* stream) {
+  if (n_req < 0 || H <= 0 || L < 1 || blocks_per_req < 1) return KDA_ERR_INVALID_ARG;
+  if (L > 256) return KDA_ERR_UNSUPPORTED;
+  if (block_size <= L) return KDA_ERR_INVALID_ARG;   // a window would close more than one block
+  if (!dtype_ok(rec_dtype)) return KDA_ERR_UNSUPPORTED;
+  if (d_k != 128 || d_v != 128) return KDA_ERR_UNSUPPORTED;
+  kda_status ps = check_pool(pool, H, d_k, d_v);
+  if (ps != KDA_OK) return ps;
+  if (n_req == 0) return KDA_OK;
+  if (block_table == nullptr || num_tokens == nullptr || accepted_len == nullptr || u_rec == nullptr ||
+      kg_rec == nullptr)
+    return KDA_ERR_INVALID_ARG;
+  if ((int64_t)n_req * H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  kda::CommitAlignArgs a{pool_desc(pool), block_table, blocks_per_req, num_tokens, accepted_len, block_size,
+                         u_rec, kg_rec, rec_dtype, n_req, L, H, d_k, dev_err};
+  return launched(kda::launch_commit_align(a, static_cast<hipStream_t>(stream)));
+}
+
 kda_status kda_state_copy(kda_pool pool, const int32_t* src_slot, const int32_t* dst_slot,
                           int32_t n_pairs, int32_t* dev_err, void* stream) {
   if (n_pairs < 0) return KDA_ERR_INVALID_ARG;

@@ -63,6 +63,19 @@ struct CopyArgs {
   int32_t* dev_err;
 };
 
+struct CommitAlignArgs {
+  PoolDesc pool;
+  const int32_t* block_table;
+  int blocks_per_req;
+  const int32_t *num_tokens, *accepted_len;
+  int block_size;
+  const float* u_rec;
+  const void* kg_rec;
+  int rec_dtype;
+  int n_req, L, H, d;
+  int32_t* dev_err;
+};
+
 // One conv tensor of a fused conv-state update: per slot `rows` positions of
 // `dim` channels (position-major), the first `keep` rows the carried history.
 constexpr int kMaxConvTensors = 8;
@@ -94,6 +107,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
+hipError_t launch_commit_align(const CommitAlignArgs& a, hipStream_t s);
 hipError_t launch_conv_update(const ConvArgs& a, hipStream_t s);
 
 }  // namespace kda

@@ -130,6 +130,25 @@ def test_verify_commit_copy_host_errors(L):
     assert s(n=0) == 0
 
 
+def test_commit_align_host_errors(L):
+    P = pool()
+    ca = lambda **kw: L.kda_commit_align(*[kw.get(n, d) for n, d in [
+        ("pool", P), ("bt", FAKE), ("bpr", 4), ("nt", FAKE), ("acc", FAKE), ("bs", 64), ("u", FAKE),
+        ("kg", FAKE), ("rdt", 2), ("n", 4), ("L", 8), ("H", 2), ("dk", 128), ("dv", 128), ("err", None),
+        ("st", None)]])
+    assert ca(bs=8) == 1            # a window of 8 could close two blocks of 8
+    assert ca(bs=9, n=0) == 0
+    assert ca(bpr=0) == 1
+    assert ca(bt=None) == 1
+    assert ca(nt=None) == 1
+    assert ca(acc=None) == 1
+    assert ca(L=300, bs=400) == 2
+    assert ca(rdt=7) == 2
+    assert ca(dk=64, dv=64) == 2
+    assert ca(pool=pool(H=4)) == 1
+    assert ca(n=0) == 0
+
+
 def conv_tensor(base=FAKE, stride=11 * 4096 * 2, n_slots=8, rows=11, keep=3, dim=4096, eb=2):
     return kda.KdaConvTensor(base.value if base is not None else None, stride, n_slots, rows, keep, dim, eb)
 
