@@ -241,6 +241,25 @@ def main():
         kda.state_copy(sp["pool"], i32(ck, dev), i32(fresh, dev))
         torch.cuda.synchronize()
 
+    # achievable-bandwidth reference: a plain 1 GiB device-to-device copy
+    # (torch's copy kernel), read + write counted; context only, the roofline
+    # fractions are taken against the published 8 TB/s
+    ref_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    ref_dst = torch.empty_like(ref_src)
+    ref_src.fill_(1)
+    ref_dst.copy_(ref_src)
+    e0, e1 = ev(), ev()
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(5):
+        ref_dst.copy_(ref_src)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ref_ms = e0.elapsed_time(e1) / 5
+    hbm_reference = {"copy_bytes": 2 << 30, "ms": ref_ms, "GBps": (2 << 30) / (ref_ms * 1e-3) / 1e9,
+                     "note": "1 GiB device-to-device copy, read + write counted"}
+    del ref_src, ref_dst
+
     def spread(x):
         return {"median": float(np.median(x)), "p10": float(np.percentile(x, 10)),
                 "p90": float(np.percentile(x, 90))}
@@ -277,6 +296,7 @@ def main():
         **{c: {"ms": ms[c], "ms_spread": spread(per[c]), "GBps": gbs[c], "hbm_frac": gbs[c] * 1e9 / HBM_PEAK}
            for c in state_calls},
         "roofline": roof,
+        "hbm_reference": hbm_reference,
         "cold": None if cold is None else {
             "note": "L2 and MALL flushed by a 512 MiB write before each step",
             "steps": a.cold_steps,
