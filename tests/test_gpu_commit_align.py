@@ -51,7 +51,7 @@ def run_case(pool_dtype, block_size, p, n, H=4, L=8, blocks=4, seed=61):
                 table=table, ck=ck)
 
 
-@pytest.mark.parametrize("pool_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("pool_dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("block_size", [9, 12, 64])
 def test_commit_align_matches_oracle(pool_dtype, block_size):
     bs = block_size
@@ -97,4 +97,20 @@ def test_commit_align_errors():
     assert written == {int(r["table"][3][1])}
     for slot in range(r["pool"].shape[0]):
         if slot not in written:
+            assert torch.equal(r["pool"][slot], r["before"][slot]), slot
+
+
+def test_commit_align_short_window():
+    """L = 3, block size 4 (the smallest allowed): every request crosses or
+    touches a block end."""
+    bs, L = 4, 3
+    p = [1, 2, 3, 4, 5, 6, 7, 8]
+    n = [3, 3, 2, 1, 3, 0, 2, 3]
+    r = run_case("f32", bs, p, n, L=L, seed=64)
+    assert r["err"] == 0 and r["want_err"] == 0
+    written = set(r["writes"])
+    for slot in range(r["pool"].shape[0]):
+        if slot in written:
+            assert rel_per_head(to_math(r["pool"][slot]), r["writes"][slot], 0) < 1e-4, slot
+        else:
             assert torch.equal(r["pool"][slot], r["before"][slot]), slot

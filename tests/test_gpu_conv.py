@@ -83,6 +83,15 @@ def test_conv_speculative_decode_shape():
     assert run_and_check(ts, keep, case["fork_dst"].tolist(), case["fork_src"].tolist(), [0] * n) == 0
 
 
+def test_conv_whole_slot_copy():
+    """keep == rows: a copy moves the whole window; no shift is valid."""
+    t = rand_bits((6, 4, 128), torch.bfloat16, 6)
+    u = rand_bits((6, 4, 32), torch.float32, 7)
+    dst, src, shift = [1, 2, 3, 4], [0, -1, 5, 5], [0, 0, 1, 0]
+    e = run_and_check([t, u], [4, 4], dst, src, shift)
+    assert e == kda.DEV_ERR_SHIFT
+
+
 def test_conv_no_ops():
     t = rand_bits((4, 5, 64), torch.bfloat16, 5)
     before = bits(t)
