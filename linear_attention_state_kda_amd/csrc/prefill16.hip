@@ -17,7 +17,8 @@
 //  * kda_chunk_prep16: one workgroup per (chunk, head), fully parallel;
 //    writes the record as MFMA A-operand fragment blocks.
 //  * kda_chunk_scan16: one workgroup per (sequence, head, 16-column tile of
-//    S); four chain waves carry the fp32 state, four output waves compute O.
+//    S); four chain waves carry the fp32 state, four output waves compute O,
+//    and a ninth wave pulls records into the L2 ahead of them.
 #include "prefill_common.hpp"
 
 namespace kda {
@@ -398,7 +399,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
 
 // ---------------------------------------------------------------- scan
 //
-// Eight waves per (sequence, head, 16-column tile of S), two per SIMD.
+// Nine waves per (sequence, head, 16-column tile of S): eight that compute,
+// two per SIMD, and one that only warms the L2.
 //  * Chain waves 0-3: wave w holds the fp32 state rows of key tiles 2w and
 //    2w + 1 (keys 32w .. 32w+31 in the accumulator layout: lane (g, r) has
 //    keys 4g + e of a tile, column r) and token tile w.  Per chunk:
@@ -412,6 +414,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
 //    O += Pw Y after barrier 2, then the tile goes to o.  They also move the
 //    next chunk's V tile and e^Gamma_n into LDS.
 //  * Each wave loads its share of a record two chunks ahead into registers.
+//  * Prefetch wave 8: the NVT workgroups of a head read every line of every
+//    record, and the first of them to ask for a line waits for the memory
+//    side while the others queue behind that miss.  Each workgroup's wave 8
+//    touches its own eighth of the record (one dword per 128-byte line)
+//    kScanPrefetch chunks ahead and waits for those loads itself, so the
+//    lines are in the XCD's L2 by the time the other waves ask; no other
+//    wave's wait counts include these loads.
+constexpr int kScanThreads = 9 * 64;
+constexpr int kScanPrefetch = 4;   // chunks ahead of the one being scanned
+
 template <typename TIn>
 struct Scan16Lds {
   uint4 sf[4][64];          // S as B fragments, key block w from chain wave w
@@ -422,7 +434,7 @@ struct Scan16Lds {
 };
 
 template <typename TIn, typename TPool>
-__global__ __launch_bounds__(512) void kda_chunk_scan16(
+__global__ __launch_bounds__(kScanThreads) void kda_chunk_scan16(
     const TIn* __restrict__ v, TIn* __restrict__ o, const int32_t* __restrict__ cu, int n_seqs,
     int64_t total, int H, int64_t cap, const int32_t* __restrict__ off, const uint8_t* __restrict__ recs,
     TPool* __restrict__ pool, int64_t n_slots, const int32_t* __restrict__ init_slot,
@@ -460,7 +472,7 @@ __global__ __launch_bounds__(512) void kda_chunk_scan16(
     }
   }
   if (lead) {
-    for (int e = e0 + tid; e < e1; e += 512) {
+    for (int e = e0 + tid; e < e1; e += kScanThreads) {
       const int ce = track_chunk[e], se = track_slot[e];
       if (ce < 0 || ce > len / C) set_err(dev_err, 1u << 1);
       if (se < -1 || (int64_t)se >= n_slots) set_err(dev_err, 1u);
@@ -579,6 +591,26 @@ __global__ __launch_bounds__(512) void kda_chunk_scan16(
     } else if (fs != -1 && lead && tid == 0) {
       set_err(dev_err, 1u);
     }
+  } else if (wv == 8) {
+    // ---- prefetch wave: lane l touches line l of share vt (one of NVT) of
+    //      a record (lanes past the share or the record read nothing), and
+    //      consumes each step's load two steps later
+    constexpr int kLines = (R::kBytes / 128 + NVT - 1) / NVT;
+    static_assert(kLines <= kWave, "one line per lane");
+    const int line = vt * kLines + lane;
+    const int poff = lane < kLines && line * 128 < R::kBytes ? line * 128 : 0x7fffff00;  // out of range: no access
+    auto touch = [&](int c) { return __builtin_amdgcn_raw_buffer_load_b32(rec_rsrc(min(c, last)), poff, 0, 0); };
+    uint32_t pa = touch(kScanPrefetch - 2), pb = touch(kScanPrefetch - 1);
+    for (int c = 0; c < nch; ++c) {   // two barriers per chunk, as in the other waves
+      __syncthreads();
+      asm volatile("" ::"v"(pa));     // the load of two steps ago has returned
+      pa = touch(c + kScanPrefetch);
+      __syncthreads();
+      const uint32_t t = pa;
+      pa = pb;
+      pb = t;
+    }
+    asm volatile("" ::"v"(pa), "v"(pb));
   } else if (nch > 0) {
     // ---- output waves, token tile m = w
     const int m = w;
@@ -677,7 +709,7 @@ hipError_t run16(const PrefillArgs& a, hipStream_t st, int64_t cap, const int32_
     hipError_t e = hipFuncSetAttribute((const void*)ks, hipFuncAttributeMaxDynamicSharedMemorySize, lds_pad);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(ks, dim3((unsigned)blocks), dim3(512), lds_pad, st,
+  hipLaunchKernelGGL(ks, dim3((unsigned)blocks), dim3(kScanThreads), lds_pad, st,
                      static_cast<const TIn*>(a.v), static_cast<TIn*>(a.o), a.cu_seqlens, a.n_seqs,
                      a.total_tokens, a.H, cap, off, recs, static_cast<TPool*>(a.pool.base),
                      a.pool.n_slots, a.init_slot, a.final_slot, a.track_ptr, a.track_chunk,
