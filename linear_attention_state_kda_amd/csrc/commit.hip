@@ -85,11 +85,23 @@ __device__ __forceinline__ void load_state(floatx4 (&S)[kRows], const TPool* sp)
 #pragma unroll
   for (int j = 0; j < kRows; ++j) S[j] = load4(sp + (r0 + 8 * j) * kD + 4 * kq);
 }
+// The rebuilt state is stored non-temporally: nothing reads it again within
+// this call, and ordinary stores of a whole batch of states (about 0.5 GB at
+// 256 requests x 32 heads) leave that much dirty data in the memory-side
+// cache, which the next kernel then pays to write back while it streams its
+// own reads (a verify right after a commit of the same checkpoints took
+// 175 us instead of 149 us).
 template <typename TPool>
 __device__ __forceinline__ void store_state(TPool* dp, const floatx4 (&S)[kRows]) {
+  typedef typename Vec4<TPool>::type V;
   const int kq = threadIdx.x & 31, r0 = threadIdx.x >> 5;
 #pragma unroll
-  for (int j = 0; j < kRows; ++j) store4(dp + (r0 + 8 * j) * kD + 4 * kq, S[j]);
+  for (int j = 0; j < kRows; ++j) {
+    V x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = from_f32<TPool>(S[j][e]);
+    __builtin_nontemporal_store(x, reinterpret_cast<V*>(dp + (r0 + 8 * j) * kD + 4 * kq));
+  }
 }
 
 template <typename TPool, typename TRec>
