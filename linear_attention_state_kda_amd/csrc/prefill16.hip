@@ -116,7 +116,7 @@ __device__ __forceinline__ void put_half(void* slot, int hf, floatx4 x) {
 // give the phases that hold each view).
 struct Prep16Smem {
   union {
-    uint4 kh[4][4][64];        // Kh fragments [token tile][channel block][lane]    (Kh, P/M)
+    uint4 kh[4][4][64];        // Kh fragments [token tile][channel block][lane]    (Kh, P/M; then Z assembly)
     struct {
       float nd[4][16][20];     // diagonal N blocks, row-major                        (T solve)
       floatx4 nr[6][64];       // row forms of N_im, m < i, at i (i - 1) / 2 + m
@@ -125,7 +125,7 @@ struct Prep16Smem {
   } r1;
   union {
     uint4 stage[4][16][17];    // input rows [wave][row][16-byte piece], padded       (inputs)
-    uint4 kbt[8][2][64];       // Kb^T fragments [key tile][token block][lane]        (Kb^T, Z)
+    uint4 kbt[8][2][64];       // Kb^T fragments [key tile][token block][lane]        (Kb^T, Z; then Pw assembly)
   } r2;
   union {
     struct {
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
       const float gn = a0 + a1 + a2 + a3;
       sm.r3.g.gn[ch] = gn;
       sm.r3.g.ninv[ch] = __expf(-gn);
-      reinterpret_cast<float*>(rec + R::kDec)[ch] = __expf(gn);
+      __builtin_nontemporal_store(__expf(gn), reinterpret_cast<float*>(rec + R::kDec) + ch);  // whole lines
     }
   }
   __syncthreads();
@@ -274,10 +274,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
         khf[kb][4 * hf + e] = from_f32<T>(kbv * ni[e]);
       }
     }
+  // Records are stored non-temporally, in whole 16-byte fragment pieces
+  // (Z and Pw are assembled in LDS first): the scan reads each record once,
+  // about a prep's duration later, and dirty records left in the
+  // memory-side cache cost the next kernel their write-back (a verify right
+  // after the prefill 147 -> 134 us).  Non-temporal 8-byte halves, each
+  // line completed by a second wave, made the prefill slower instead.
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int kb = 0; kb < NFK; ++kb) {
-    *reinterpret_cast<F8*>(rec + R::kKt + (w * NFK + kb) * kFB + lane * 16) = ktf[kb];
-    *reinterpret_cast<F8*>(rec + R::kQt + (w * NFK + kb) * kFB + lane * 16) = qtf[kb];
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, ktf[kb]),
+                                reinterpret_cast<u32x4*>(rec + R::kKt + (w * NFK + kb) * kFB + lane * 16));
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, qtf[kb]),
+                                reinterpret_cast<u32x4*>(rec + R::kQt + (w * NFK + kb) * kFB + lane * 16));
     sm.r1.kh[w][kb][lane] = __builtin_bit_cast(uint4, khf[kb]);
   }
   // 0/1 selection fragments: sel[hf] picks channel 16 hf + r of a K-block, so
@@ -375,6 +384,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   F8 ta[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) ta[b] = pack8<T>(tc[2 * b], tc[2 * b + 1]);
+  // Z and Pw halves are assembled in LDS (Z over the T solve's space, Pw over
+  // Kb^T's once Z is done), then stored as whole 16-byte pieces
+  uint4* const zst = &sm.r1.kh[0][0][0];       // 16 blocks x 64 lanes
+  uint4* const pst = &sm.r2.kbt[0][0][0];      //  6 blocks x 64 lanes
+  __syncthreads();   // every wave is done with the T solve's LDS
   const floatx4 bw = *reinterpret_cast<const floatx4*>(&sm.beta[16 * w + 4 * gq]);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -382,10 +396,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
 #pragma unroll
     for (int b = 0; b < 2; ++b)
       if (b >= w / 2) acc = mma(acc, ta[b], __builtin_bit_cast(F8, sm.r2.kbt[i][b][lane]));
-    put_half<T>(rec + R::kZ + (2 * i + (w >> 1)) * kFB + lane * 16, w & 1, bw * acc);
+    put_half<T>(reinterpret_cast<uint8_t*>(zst) + (2 * i + (w >> 1)) * kFB + lane * 16, w & 1, bw * acc);
   }
+  floatx4 pw_acc[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
+    pw_acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
     if (m / 2 < w / 2) continue;  // block (m, w / 2) lies above the diagonal
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     if (m >= w) {  // else the upper half of a diagonal block: zero
@@ -393,7 +409,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
       for (int b = 0; b < 2; ++b)
         if (b >= w / 2 && b <= m / 2) acc = mma(acc, ta[b], __builtin_bit_cast(F8, sm.r3.p[pw_blk(m) + b][lane]));
     }
-    put_half<T>(rec + R::kPw + (pw_blk(m) + (w >> 1)) * kFB + lane * 16, w & 1, bw * acc);
+    pw_acc[m] = bw * acc;
+  }
+  __syncthreads();   // Z assembled; Kb^T no longer read
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    if (m / 2 < w / 2) continue;
+    put_half<T>(reinterpret_cast<uint8_t*>(pst) + (pw_blk(m) + (w >> 1)) * kFB + lane * 16, w & 1, pw_acc[m]);
+  }
+  typedef unsigned int u32x4s __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {   // wave w stores Z blocks 4 w .. 4 w + 3
+    const uint4 x = zst[(4 * w + jb) * 64 + lane];
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4s, x),
+                                reinterpret_cast<u32x4s*>(rec + R::kZ + (4 * w + jb) * kFB + lane * 16));
+  }
+  __syncthreads();   // Pw assembled
+  for (int jb = w; jb < 6; jb += 4) {
+    const uint4 x = pst[jb * 64 + lane];
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4s, x),
+                                reinterpret_cast<u32x4s*>(rec + R::kPw + jb * kFB + lane * 16));
   }
 }
 
