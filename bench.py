@@ -8,12 +8,15 @@ One step = one pass of the whole path over resident synthetic inputs:
     workload (256 requests, L = 8, H = 32, fp32 128 x 128 checkpoints in a
     1024-slot pool, accepted ~ U{0..8}, in-place commit, fork of 64
     committed checkpoints to 4 children each).
-value = prefill tokens/s (T / mean prefill time).  Each call is bracketed by
+value = prefill tokens/s (T / mean prefill time).  An informational leg
+outside the step times the same prefill on the varlen batch (16 sequences,
+lengths ~ U[512, 16384]) and reports it as `prefill_varlen`.  Each call is
+bracketed by
 HIP events on the stream it is launched on; the roofline object covers the
 call that dominates the step.  The cpu_baseline leg times the fp64 oracle
 (single thread) on the first tokens of the same prefill workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-varlen]
 """
 
 import argparse
@@ -115,6 +118,43 @@ def spec_setup(dev):
                            conv_fork=conv_op_bytes * n_fork))
 
 
+def varlen_setup(dev):
+    """The varlen prefill batch (16 packed sequences, lengths ~ U[512, 16384],
+    H = 32, d = 128, chunk 64, bf16 inputs, 1024-slot fp32 pool, initial
+    states from pool slots, one fp32 snapshot per sequence), drawn with torch's
+    generator on the device: the same distributions as the seeded workload,
+    without its fp64 host pass (this leg is timed, not checked)."""
+    case = wl.varlen_prefill("f32")
+    lengths = np.asarray(case["lengths"], dtype=np.int64)
+    T, H, d, C = int(lengths.sum()), case["H"], case["dk"], case["chunk"]
+    gen = torch.Generator(device=dev).manual_seed(case["seed"])
+
+    def unit(x):
+        return x / x.norm(dim=-1, keepdim=True)
+    t = {"q": unit(torch.randn((T, H, d), generator=gen, device=dev)),
+         "k": unit(torch.randn((T, H, d), generator=gen, device=dev)),
+         "v": torch.randn((T, H, d), generator=gen, device=dev),
+         "g": torch.empty((T, H, d), device=dev).uniform_(-0.1, -0.001, generator=gen),
+         "b": torch.randn((T, H), generator=gen, device=dev)}
+    t = {n: x.to(torch.bfloat16) for n, x in t.items()}
+    pool = torch.randn((case["n_slots"], H, d, d), generator=gen, device=dev)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    tr = sorted(case["tracks"])
+    ptr = np.searchsorted([s_ for s_, _, _ in tr], np.arange(len(lengths) + 1)).astype(np.int32)
+    args = dict(q=t["q"], k=t["k"], v=t["v"], g=t["g"], b=t["b"], cu_seqlens=i32(cu, dev), chunk=C,
+                pool=pool, init_slot=i32(case["init_slots"], dev), final_slot=i32(case["final_slots"], dev),
+                track_ptr=i32(ptr, dev), track_chunk=i32([c for _, c, _ in tr], dev),
+                track_slot=i32([sl for _, _, sl in tr], dev),
+                track_f32=torch.empty((len(tr), H, d, d), dtype=torch.float32, device=dev),
+                o=torch.empty((T, H, d), dtype=torch.bfloat16, device=dev))
+    args["workspace"] = torch.empty(kda.prefill_workspace_bytes(len(lengths), T, H, d, d, C, torch.bfloat16),
+                                    dtype=torch.uint8, device=dev)
+    # per sequence-head: init read, final write, snapshot into the pool and the fp32 copy
+    bytes_ = T * H * (4 * d * 2 + 2 + d * 2) + len(lengths) * H * d * d * 4 * 4
+    flops = T * H * (6 * d * d + 5 * C * d)
+    return args, T, len(lengths), bytes_, flops
+
+
 def measured_prefill_traffic():
     """HBM bytes per prefill call from the committed FETCH_SIZE / WRITE_SIZE
     profile (already scaled by the copy calibration), or None when the
@@ -164,6 +204,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="extra steps, each after a 512 MiB cache-flushing write (0 to skip)")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the informational varlen prefill leg (16 sequences, 135k tokens)")
     ap.add_argument("--traffic-calibration", action="store_true",
                     help="after the timed steps, run one kda_state_copy of 256 distinct fp32 "
                          "slots (512 MiB read + 512 MiB written) so that FETCH_SIZE / WRITE_SIZE "
@@ -235,6 +277,27 @@ def main():
         cold = {c: np.array([cevs[s][i].elapsed_time(cevs[s][i + 1]) for s in range(a.cold_steps)])
                 for i, c in enumerate(calls)}
         del scratch
+    # Informational leg, outside the step and `value`: the same prefill
+    # kernels on the varlen batch, where 16 sequences give the scan 16x more
+    # independent chains than the single-layer workload's one.
+    varlen = None
+    if not a.no_varlen:
+        vargs, vT, vn, vbytes, vflops = varlen_setup(dev)
+        for _ in range(2):
+            kda.chunk_prefill(**vargs)
+        vev = [[ev(), ev()] for _ in range(5)]
+        for e0, e1 in vev:
+            e0.record(st)
+            kda.chunk_prefill(**vargs)
+            e1.record(st)
+        torch.cuda.synchronize()
+        vms = float(np.median([e0.elapsed_time(e1) for e0, e1 in vev]))
+        varlen = {"workload": f"varlen prefill, {vn} sequences, {vT} tokens, H=32, d=128, chunk 64, "
+                              "bf16, fp32 pool, pool initial states, one snapshot per sequence",
+                  "ms_median": vms, "tokens_per_s": vT / (vms * 1e-3),
+                  "hbm_GBps": vbytes / (vms * 1e-3) / 1e9, "hbm_frac": vbytes / (vms * 1e-3) / HBM_PEAK,
+                  "mfma_TFLOPs": vflops / (vms * 1e-3) / 1e12, "mfma_frac": vflops / (vms * 1e-3) / BF16_PEAK}
+        del vargs
     if a.traffic_calibration:
         ck = sp["case"]["ckpt_slots"]
         fresh = sorted(set(range(sp["case"]["n_slots"])) - set(ck.tolist()))[:len(ck)]
@@ -303,6 +366,7 @@ def main():
             **{c: {"ms_median": float(np.median(cold[c])), "ms_p10": float(np.percentile(cold[c], 10)),
                    "ms_p90": float(np.percentile(cold[c], 90))} for c in calls},
             "prefill_tokens_per_s": T / (float(np.median(cold["prefill"])) * 1e-3)},
+        "prefill_varlen": varlen,
         "device": torch.cuda.get_device_name(0),
     }
     if not a.no_cpu_baseline:

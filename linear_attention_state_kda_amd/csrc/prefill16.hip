@@ -16,8 +16,9 @@
 // Two launches after the chunk map (prefill.hip):
 //  * kda_chunk_prep16: one workgroup per (chunk, head), fully parallel;
 //    writes the record as MFMA A-operand fragment blocks.
-//  * kda_chunk_scan16: one workgroup per (sequence, head, 16-column tile of
-//    S); four chain waves carry the fp32 state, four output waves compute O,
+//  * kda_chunk_scan16: one workgroup per (sequence, head, column tile of S:
+//    16, 32 or 64 columns, by how many (sequence, head) pairs there are);
+//    four chain waves carry the fp32 state, four output waves compute O,
 //    and a ninth wave pulls records into the L2 ahead of them.
 #include "prefill_common.hpp"
 
@@ -434,8 +435,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
 
 // ---------------------------------------------------------------- scan
 //
-// Nine waves per (sequence, head, 16-column tile of S): eight that compute,
-// two per SIMD, and one that only warms the L2.
+// Nine waves per (sequence, head, column tile of S): eight that compute,
+// two per SIMD, and one that only warms the L2.  A tile is NC 16-column
+// tiles (NC = 1, 2 or 4): every product below runs once per 16-column tile,
+// on the same record fragments.  One sequence's 32 heads give 256 narrow
+// tiles, one per CU, which keeps the most CUs on the serial chain; with many
+// sequences, wider tiles mean fewer passes over each record.
 //  * Chain waves 0-3: wave w holds the fp32 state rows of key tiles 2w and
 //    2w + 1 (keys 32w .. 32w+31 in the accumulator layout: lane (g, r) has
 //    keys 4g + e of a tile, column r) and token tile w.  Per chunk:
@@ -459,16 +464,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
 constexpr int kScanThreads = 9 * 64;
 constexpr int kScanPrefetch = 4;   // chunks ahead of the one being scanned
 
-template <typename TIn>
+template <typename TIn, int NC>
 struct Scan16Lds {
-  uint4 sf[4][64];          // S as B fragments, key block w from chain wave w
-  uint4 y[2][64];           // Y as B fragments, token block b
+  uint4 sf[NC][4][64];      // S as B fragments per 16-column tile, key block w from chain wave w
+  uint4 y[NC][2][64];       // Y as B fragments per 16-column tile, token block b
   float dec[2][128];        // e^Gamma_n, by chunk parity
-  TIn vb[2][64][16];        // V tiles, row-major, by chunk parity
-  TIn ob[4][16][16];        // one output tile per output wave
+  TIn vb[2][64][16 * NC];   // V tiles, row-major, by chunk parity
+  TIn ob[4][16][16 * NC];   // one output tile per output wave
 };
 
-template <typename TIn, typename TPool>
+template <typename TIn, typename TPool, int NC>
 __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan16(
     const TIn* __restrict__ v, TIn* __restrict__ o, const int32_t* __restrict__ cu, int n_seqs,
     int64_t total, int H, int64_t cap, const int32_t* __restrict__ off, const uint8_t* __restrict__ recs,
@@ -476,10 +481,10 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan16(
     const int32_t* __restrict__ final_slot, const int32_t* __restrict__ track_ptr,
     const int32_t* __restrict__ track_chunk, const int32_t* __restrict__ track_slot, int n_track,
     float* __restrict__ track_f32, int32_t* __restrict__ dev_err) {
-  constexpr int DK = 128, DV = 128, C = 64, BV = 16, NVT = DV / BV;
+  constexpr int DK = 128, DV = 128, C = 64, BV = 16 * NC, NVT = DV / BV;
   typedef Rec16 R;
   typedef typename OpTraits<TIn>::frag F8;
-  __shared__ Scan16Lds<TIn> sm;
+  __shared__ Scan16Lds<TIn, NC> sm;
 
   const int tid = threadIdx.x, lane = tid & 63, g16 = lane >> 4, l16 = lane & 15;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
@@ -529,20 +534,24 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan16(
 
   if (chain) {
     // ---- initial state of key tiles 2w, 2w + 1: S[k][v] = pool[init][h][v][k]
-    floatx4 S[2];
-    const int64_t st_off = (int64_t)(v0 + l16) * DK + 32 * w + 4 * g16;  // lane's first element
+    floatx4 S[NC][2];
+    const int64_t st_off = (int64_t)(v0 + l16) * DK + 32 * w + 4 * g16;  // lane's first element (tile 0)
     {
       const int is = init_slot[seq];
       const bool ok = is >= 0 && (int64_t)is < n_slots;
       if (is != -1 && !ok && lead && tid == 0) set_err(dev_err, 1u);
       const TPool* src = pool + ((int64_t)(ok ? is : 0) * H + h) * DV * DK + st_off;
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        S[jj] = floatx4{0.f, 0.f, 0.f, 0.f};
-        if (ok) S[jj] = load4(src + 16 * jj);
-      }
+      for (int ct = 0; ct < NC; ++ct)
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) asm volatile("" : "+v"(S[jj]));
+        for (int jj = 0; jj < 2; ++jj) {
+          S[ct][jj] = floatx4{0.f, 0.f, 0.f, 0.f};
+          if (ok) S[ct][jj] = load4(src + 16 * ct * DK + 16 * jj);
+        }
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) asm volatile("" : "+v"(S[ct][jj]));
     }
     // Snapshots: `next_snap` is the smallest requested chunk index >= the
     // current one, so the per-chunk test is one scalar compare.
@@ -562,10 +571,13 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan16(
         const int se = track_slot[e];
         const bool to_pool = se >= 0 && (int64_t)se < n_slots;
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          if (track_f32) store4(track_f32 + ((int64_t)e * H + h) * DV * DK + st_off + 16 * jj, S[jj]);
-          if (to_pool) store4(pool + ((int64_t)se * H + h) * DV * DK + st_off + 16 * jj, S[jj]);
-        }
+        for (int ct = 0; ct < NC; ++ct)
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int64_t el = st_off + 16 * ct * DK + 16 * jj;
+            if (track_f32) store4(track_f32 + ((int64_t)e * H + h) * DV * DK + el, S[ct][jj]);
+            if (to_pool) store4(pool + ((int64_t)se * H + h) * DV * DK + el, S[ct][jj]);
+          }
       }
       next_snap = next_track(c + 1);
     };
@@ -583,24 +595,36 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan16(
       snapshot(c);
       __syncthreads();
       // X = Kt S for token tile w;  Y = V - X
-      floatx4 X = {0.f, 0.f, 0.f, 0.f};
+      floatx4 X[NC];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) X = mma(X, as_frag<F8>(r.kt[f]), __builtin_bit_cast(F8, sm.sf[f][lane]));
-      floatx4 Y;
+      for (int ct = 0; ct < NC; ++ct) {
+        X[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Y[e] = to_f32(sm.vb[bp][16 * w + 4 * g16 + e][l16]) - X[e];
-      put_half<TIn>(&sm.y[w >> 1][lane], w & 1, Y);
+        for (int f = 0; f < 4; ++f) X[ct] = mma(X[ct], as_frag<F8>(r.kt[f]), __builtin_bit_cast(F8, sm.sf[ct][f][lane]));
+      }
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) {
+        floatx4 Y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Y[e] = to_f32(sm.vb[bp][16 * w + 4 * g16 + e][16 * ct + l16]) - X[ct][e];
+        put_half<TIn>(&sm.y[ct][w >> 1][lane], w & 1, Y);
+      }
       __syncthreads();
       // S = e^Gamma_n S + Z Y
-      const F8 y0 = __builtin_bit_cast(F8, sm.y[0][lane]), y1 = __builtin_bit_cast(F8, sm.y[1][lane]);
+      floatx4 dec[2];
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        floatx4 acc = mma(floatx4{0.f, 0.f, 0.f, 0.f}, as_frag<F8>(r.z[jj][0]), y0);
-        acc = mma(acc, as_frag<F8>(r.z[jj][1]), y1);
-        const floatx4 dec = *reinterpret_cast<const floatx4*>(&sm.dec[bp][32 * w + 16 * jj + 4 * g16]);
-        S[jj] = dec * S[jj] + acc;
+      for (int jj = 0; jj < 2; ++jj) dec[jj] = *reinterpret_cast<const floatx4*>(&sm.dec[bp][32 * w + 16 * jj + 4 * g16]);
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) {
+        const F8 y0 = __builtin_bit_cast(F8, sm.y[ct][0][lane]), y1 = __builtin_bit_cast(F8, sm.y[ct][1][lane]);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          floatx4 acc = mma(floatx4{0.f, 0.f, 0.f, 0.f}, as_frag<F8>(r.z[jj][0]), y0);
+          acc = mma(acc, as_frag<F8>(r.z[jj][1]), y1);
+          S[ct][jj] = dec[jj] * S[ct][jj] + acc;
+        }
+        sm.sf[ct][w][lane] = __builtin_bit_cast(uint4, pack8<TIn>(S[ct][0], S[ct][1]));
       }
-      sm.sf[w][lane] = __builtin_bit_cast(uint4, pack8<TIn>(S[0], S[1]));
       ld_ops(r, min(c + 2, last));
     };
 
@@ -608,7 +632,8 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan16(
       Ops rA, rB;
       ld_ops(rA, 0);
       ld_ops(rB, min(1, last));
-      sm.sf[w][lane] = __builtin_bit_cast(uint4, pack8<TIn>(S[0], S[1]));
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) sm.sf[ct][w][lane] = __builtin_bit_cast(uint4, pack8<TIn>(S[ct][0], S[ct][1]));
       int c = 0;
       for (; c + 1 < nch; c += 2) {
         step(rA, c, 0);
@@ -622,7 +647,10 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan16(
     const int fs = final_slot[seq];
     if (fs >= 0 && (int64_t)fs < n_slots) {
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) store4(pool + ((int64_t)fs * H + h) * DV * DK + st_off + 16 * jj, S[jj]);
+      for (int ct = 0; ct < NC; ++ct)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+          store4(pool + ((int64_t)fs * H + h) * DV * DK + st_off + 16 * ct * DK + 16 * jj, S[ct][jj]);
     } else if (fs != -1 && lead && tid == 0) {
       set_err(dev_err, 1u);
     }
@@ -631,32 +659,61 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan16(
     //      a record (lanes past the share or the record read nothing), and
     //      consumes each step's load two steps later
     constexpr int kLines = (R::kBytes / 128 + NVT - 1) / NVT;
-    static_assert(kLines <= kWave, "one line per lane");
-    const int line = vt * kLines + lane;
-    const int poff = lane < kLines && line * 128 < R::kBytes ? line * 128 : 0x7fffff00;  // out of range: no access
-    auto touch = [&](int c) { return __builtin_amdgcn_raw_buffer_load_b32(rec_rsrc(min(c, last)), poff, 0, 0); };
-    uint32_t pa = touch(kScanPrefetch - 2), pb = touch(kScanPrefetch - 1);
+    constexpr int NPL = (kLines + kWave - 1) / kWave;   // loads per step
+    int poff[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int li = kWave * i + lane, line = vt * kLines + li;
+      poff[i] = li < kLines && line * 128 < R::kBytes ? line * 128 : 0x7fffff00;  // out of range: no access
+    }
+    auto touch = [&](uint32_t (&x)[NPL], int c) {
+      const auto rs = rec_rsrc(min(c, last));
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) x[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, poff[i], 0, 0);
+    };
+    uint32_t pa[NPL], pb[NPL];
+    touch(pa, kScanPrefetch - 2);
+    touch(pb, kScanPrefetch - 1);
     for (int c = 0; c < nch; ++c) {   // two barriers per chunk, as in the other waves
       __syncthreads();
-      asm volatile("" ::"v"(pa));     // the load of two steps ago has returned
-      pa = touch(c + kScanPrefetch);
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) asm volatile("" ::"v"(pa[i]));   // the loads of two steps ago have returned
+      touch(pa, c + kScanPrefetch);
       __syncthreads();
-      const uint32_t t = pa;
-      pa = pb;
-      pb = t;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        const uint32_t t = pa[i];
+        pa[i] = pb[i];
+        pb[i] = t;
+      }
     }
-    asm volatile("" ::"v"(pa), "v"(pb));
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) asm volatile("" ::"v"(pa[i]), "v"(pb[i]));
   } else if (nch > 0) {
     // ---- output waves, token tile m = w
     const int m = w;
-    // V tile of a chunk: 16-byte pieces, two per row, 32 rows per 1 KiB load;
-    // output waves 0 and 1 load rows 32w .. 32w + 31.
-    const bool has_v = w < 2, has_dec = w == 2;
-    const int vq_row = 32 * w + (lane >> 1), vq_part = lane & 1;
-    const int vq_off = (int)((int64_t)vq_row * vrow * (int)sizeof(TIn)) + 16 * vq_part;
-    auto ld_v = [&](int c) { return ld16(rows_rsrc(v, c), vq_off, 0); };
-    auto put_v = [&](int bp, uint4 x) {
-      if (has_v) *reinterpret_cast<uint4*>(&sm.vb[bp][vq_row][8 * vq_part]) = x;
+    // V tile of a chunk: 16-byte pieces, 2 NC per row; piece q = 64 m + lane
+    // + 256 i of the output waves (NVP loads each)
+    constexpr int PPR = 2 * NC, NVP = (64 * PPR + 255) / 256;
+    const bool has_dec = w == 2;
+    int vq_off[NVP], vq_lds[NVP];
+    bool has_v[NVP];
+#pragma unroll
+    for (int i = 0; i < NVP; ++i) {
+      const int q = 64 * w + lane + 256 * i, row = q / PPR, part = q % PPR;
+      has_v[i] = q < 64 * PPR;
+      vq_off[i] = has_v[i] ? (int)((int64_t)row * vrow * (int)sizeof(TIn)) + 16 * part : 0x7fffff00;
+      vq_lds[i] = has_v[i] ? row * 16 * NC + 8 * part : 0;
+    }
+    auto ld_v = [&](uint4 (&x)[NVP], int c) {
+      const auto rs = rows_rsrc(v, c);
+#pragma unroll
+      for (int i = 0; i < NVP; ++i) x[i] = ld16(rs, vq_off[i], 0);
+    };
+    auto put_v = [&](int bp, const uint4 (&x)[NVP]) {
+#pragma unroll
+      for (int i = 0; i < NVP; ++i)
+        if (has_v[i]) *reinterpret_cast<uint4*>(&sm.vb[bp][0][0] + vq_lds[i]) = x[i];
     };
     auto ld_dec = [&](int c) { return ld16(rec_rsrc(c), lane_off, R::kDec); };  // lanes >= 32 read 0
     auto put_dec = [&](int bp, uint4 x) {
@@ -670,46 +727,66 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan16(
       r.pw[0] = ld16(rs, lane_off, R::kPw + pw_blk(m) * kFB);
       if (m >= 2) r.pw[1] = ld16(rs, lane_off, R::kPw + (pw_blk(m) + 1) * kFB);
     };
-    auto store_out = [&](floatx4 O, int c) {
+    // the output tile goes out in 16-byte pieces, 2 NC per row
+    constexpr int NSO = (32 * NC + 63) / 64;
+    auto store_out = [&](const floatx4 (&O)[NC], int c) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sm.ob[m][4 * g16 + e][l16] = from_f32<TIn>(O[e]);
+      for (int ct = 0; ct < NC; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.ob[m][4 * g16 + e][16 * ct + l16] = from_f32<TIn>(O[ct][e]);
       wave_sync();
-      if (lane < 32) {
-        const int orow = lane >> 1, opart = lane & 1;
-        const uint4 x = *reinterpret_cast<const uint4*>(&sm.ob[m][orow][8 * opart]);
-        __builtin_amdgcn_raw_buffer_store_b128(
-            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, x), rows_rsrc(o, c),
-            (int)((int64_t)(16 * m + orow) * vrow * (int)sizeof(TIn)) + 16 * opart, 0, 0);
+      const auto rs = rows_rsrc(o, c);
+#pragma unroll
+      for (int i = 0; i < NSO; ++i) {
+        const int q = lane + 64 * i;
+        if (q < 32 * NC) {
+          const int orow = q / PPR, opart = q % PPR;
+          const uint4 x = *reinterpret_cast<const uint4*>(&sm.ob[m][orow][8 * opart]);
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, x), rs,
+              (int)((int64_t)(16 * m + orow) * vrow * (int)sizeof(TIn)) + 16 * opart, 0, 0);
+        }
       }
     };
     // step c: r = chunk c's operands; vr = V_{c+1}, dr = e^Gamma_n of chunk c + 1
-    auto step = [&](Ops& r, uint4& vr, uint4& dr, int c, int bp) {
+    auto step = [&](Ops& r, uint4 (&vr)[NVP], uint4& dr, int c, int bp) {
       __syncthreads();
-      floatx4 O = {0.f, 0.f, 0.f, 0.f};
+      floatx4 O[NC];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) O = mma(O, as_frag<F8>(r.qt[f]), __builtin_bit_cast(F8, sm.sf[f][lane]));
+      for (int ct = 0; ct < NC; ++ct) {
+        O[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int f = 0; f < 4; ++f) O[ct] = mma(O[ct], as_frag<F8>(r.qt[f]), __builtin_bit_cast(F8, sm.sf[ct][f][lane]));
+      }
       put_v(bp ^ 1, vr);
-      vr = ld_v(min(c + 3, last));
+      ld_v(vr, min(c + 3, last));
       put_dec(bp ^ 1, dr);
       dr = ld_dec(min(c + 3, last));
       __syncthreads();
-      O = mma(O, as_frag<F8>(r.pw[0]), __builtin_bit_cast(F8, sm.y[0][lane]));
-      if (m >= 2) O = mma(O, as_frag<F8>(r.pw[1]), __builtin_bit_cast(F8, sm.y[1][lane]));
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) {
+        O[ct] = mma(O[ct], as_frag<F8>(r.pw[0]), __builtin_bit_cast(F8, sm.y[ct][0][lane]));
+        if (m >= 2) O[ct] = mma(O[ct], as_frag<F8>(r.pw[1]), __builtin_bit_cast(F8, sm.y[ct][1][lane]));
+      }
       ld_ops(r, min(c + 2, last));
       store_out(O, c);
     };
 
     Ops rA, rB;
-    uint4 vA, vB, dA, dB;
+    uint4 vA[NVP], vB[NVP], dA, dB;
     // prologue: V_0 and e^Gamma_n of chunk 0 into LDS; V_1, V_2, dec_1, dec_2
     // in registers, issued in the order the loop issues them so that its
     // wait counts stay partial
-    put_v(0, ld_v(0));
+    {
+      uint4 v0r[NVP];
+      ld_v(v0r, 0);
+      put_v(0, v0r);
+    }
     put_dec(0, ld_dec(0));
-    vA = ld_v(min(1, last));
+    ld_v(vA, min(1, last));
     dA = ld_dec(min(1, last));
     ld_ops(rA, 0);
-    vB = ld_v(min(2, last));
+    ld_v(vB, min(2, last));
     dB = ld_dec(min(2, last));
     ld_ops(rB, min(1, last));
     int c = 0;
@@ -732,14 +809,20 @@ hipError_t run16(const PrefillArgs& a, hipStream_t st, int64_t cap, const int32_
                        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                        static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.b), a.cu_seqlens,
                        a.n_seqs, a.total_tokens, a.H, cap, off, recs);
-  auto ks = kda_chunk_scan16<TIn, TPool>;
   const int64_t pairs = (int64_t)a.n_seqs * a.H;
-  const int64_t blocks = (pairs + kXcd - 1) / kXcd * kXcd * (128 / 16);
-  // Each workgroup streams a record per chunk through its CU's vector memory
-  // path.  When there are no more workgroups than CUs, reserve enough LDS
-  // (unused) that no two of them share a CU.
+  const int64_t pairs8 = (pairs + kXcd - 1) / kXcd * kXcd;
+  // Each workgroup streams its head's whole record per chunk through its
+  // CU's vector memory path, so the column tile width trades parallelism on
+  // the serial chain against record passes: the narrowest tiles (16, 32 or
+  // 64 columns) whose workgroups all fit on the CUs at once, else 64.
+  const int nc = pairs8 * 8 <= kNumCU ? 1 : pairs8 * 4 <= kNumCU ? 2 : 4;
+  auto ks = nc == 1 ? kda_chunk_scan16<TIn, TPool, 1>
+                    : nc == 2 ? kda_chunk_scan16<TIn, TPool, 2> : kda_chunk_scan16<TIn, TPool, 4>;
+  const int64_t blocks = pairs8 * (8 / nc);
+  // With 16-column tiles, reserve enough LDS (unused) that no two
+  // workgroups share a CU (the wider tiles' registers already ensure it).
   int lds_pad = 0;
-  if (blocks <= kNumCU) {
+  if (nc == 1) {
     lds_pad = kSpreadLds;
     hipError_t e = hipFuncSetAttribute((const void*)ks, hipFuncAttributeMaxDynamicSharedMemorySize, lds_pad);
     if (e != hipSuccess) return e;

@@ -3,7 +3,8 @@
 Cases: the tiny fp32 workload (T = 64, H = 2, d = 16, chunk 16); small
 multi-sequence bf16/fp16 runs at d = 128, chunk 64 that span several chunks,
 ragged tails, an empty and a one-token sequence, pool and zero initial
-states, and snapshots at c = 0, interior chunks and c = floor(T_i / C); the
+states, and snapshots at c = 0, interior chunks and c = floor(T_i / C), with
+16-, 32- and 64-column scan tiles (by the number of (sequence, head) pairs); the
 single-layer workload (T = 8229, H = 32) in full; the varlen workload (16
 sequences, lengths 512..16384) on sampled heads with fp32, fp16 and bf16
 pools; and device-side error reporting.
@@ -169,6 +170,23 @@ def test_small_multi_sequence(in_dtype, pool_dtype):
     g = run_gpu(case, toks, cu)
     w = check_case(case, toks, cu, g, [0, 1, 2])
     print(in_dtype, pool_dtype, "worst rel", w)
+
+
+@pytest.mark.parametrize("H,pool_dtype", [(8, "f32"), (12, "bf16"), (12, "f32")])
+def test_wide_column_tiles(H, pool_dtype):
+    """Enough (sequence, head) pairs that the scan takes wider column tiles:
+    7 x 8 = 56 pairs (32-column tiles), 7 x 12 = 84 pairs (64-column tiles);
+    every head checked against the oracle."""
+    init = [20, -1, 21, 22, -1, 23, -1]
+    final = [0, 1, 2, 3, 4, 5, 6]
+    tracks = [(0, 0, 7), (0, 2, 8), (0, 4, 9), (1, 1, 10), (4, 1, 11), (4, 2, 12), (5, 0, 13),
+              (6, 2, 14), (6, 1, -1), (3, 0, 15)]
+    case = wl.prefill_case(SMALL_LENS, H, 128, 128, 64, "bf16", pool_dtype, 24, init, final,
+                           tracks, True, seed=16)
+    toks, cu = tokens(case)
+    g = run_gpu(case, toks, cu)
+    w = check_case(case, toks, cu, g, list(range(H)))
+    print("wide tiles H", H, pool_dtype, "worst rel", w)
 
 
 def test_final_over_own_init_slot():
