@@ -81,6 +81,19 @@ typedef enum {
 
 typedef enum { KDA_F32 = 0, KDA_F16 = 1, KDA_BF16 = 2 } kda_dtype;
 
+/* Bits of the `flags` argument of kda_chunk_prefill and kda_recurrent_verify.
+ * KDA_QK_L2NORM: q and k arrive unnormalised and the kernel normalises each
+ * (token, head) row over d_k, qhat = q / sqrt(sum q^2 + 1e-6) and likewise
+ * k, computed in fp32 and rounded once (RNE) to in_dtype; the recurrence,
+ * the outputs and verify's key record all use the rounded qhat, khat, so a
+ * commit from the records replays exactly what verify computed.  This is
+ * the per-head L2 normalisation of q and k that the single-layer and
+ * varlen workloads specify, fused into the loads instead of a separate
+ * pass.  Built for the 16-bit (128, 128, 64) prefill and for verify; the
+ * fp32 (16, 16, 16) prefill returns KDA_ERR_UNSUPPORTED with it.  Other
+ * bits are rejected with KDA_ERR_INVALID_ARG. */
+#define KDA_QK_L2NORM 1u
+
 /* Bits set in *dev_err by the kernels. */
 #define KDA_DEV_ERR_SLOT 1u   /* a slot index outside [0, n_slots) (or -1 where not allowed) */
 #define KDA_DEV_ERR_TRACK 2u  /* a snapshot chunk outside [0, floor(T_i / chunk)], or a bad track_ptr */
@@ -125,6 +138,7 @@ kda_status kda_chunk_prefill_workspace(int32_t n_seqs, int64_t total_tokens, int
  *                 straight from the fp32 accumulator, written to
  *                 track_f32[e] (fp32 [n_track][H][d_v][d_k], optional) and,
  *                 unless track_slot[e] == -1, cast once into that pool slot.
+ * flags           0 or KDA_QK_L2NORM (q and k normalised inside the kernel).
  * dev_err         optional device word for the KDA_DEV_ERR_* bits.
  * workspace       device scratch of at least kda_chunk_prefill_workspace()
  *                 bytes, 256-byte aligned; its contents need no initialisation.
@@ -136,8 +150,8 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
                              const int32_t* init_slot, const int32_t* final_slot,
                              const int32_t* track_ptr, const int32_t* track_chunk,
                              const int32_t* track_slot, int32_t n_track, float* track_f32,
-                             int32_t* dev_err, void* workspace, size_t workspace_bytes,
-                             void* stream);
+                             uint32_t flags, int32_t* dev_err, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* Speculative-decode verify ([P3] step 3): per request, read the checkpoint
  * in pool slot ckpt_slot[r] (never written), run the token recurrence over
@@ -145,7 +159,8 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
  * write
  *   o       [n_req][L][H][d_v] in in_dtype,
  *   u_rec   [n_req][H][L][d_v] fp32 correction u_t (beta folded in),
- *   kg_rec  [n_req][H][L][2*d_k] in in_dtype: key k_t then raw gate g_t.
+ *   kg_rec  [n_req][H][L][2*d_k] in in_dtype: key k_t then raw gate g_t
+ *           (with KDA_QK_L2NORM in flags, the normalised key).
  * 1 <= L <= 256.  q, k, v, g, o, u_rec and kg_rec must be 16-byte aligned
  * (KDA_ERR_INVALID_ARG otherwise).  A request whose ckpt_slot is outside
  * [0, n_slots) sets KDA_DEV_ERR_SLOT in *dev_err and its outputs are left
@@ -154,7 +169,7 @@ kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, con
                                 const void* b, int32_t in_dtype, void* o, int32_t n_req,
                                 int32_t L, int32_t H, int32_t d_k, int32_t d_v, kda_pool pool,
                                 const int32_t* ckpt_slot, float* u_rec, void* kg_rec,
-                                int32_t* dev_err, void* stream);
+                                uint32_t flags, int32_t* dev_err, void* stream);
 
 /* RecoverSSM commit ([P3] step 4): rebuild, without re-running the
  * recurrence, the state after accepted_len[r] = n positions,

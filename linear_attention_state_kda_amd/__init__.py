@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "KdaError", "lib", "DTYPE_CODES", "DEV_ERR_SLOT", "DEV_ERR_TRACK", "DEV_ERR_ACCEPT",
-    "DEV_ERR_SEQLEN", "DEV_ERR_SHIFT", "prefill_workspace_bytes", "chunk_prefill", "recurrent_verify",
+    "DEV_ERR_SEQLEN", "DEV_ERR_SHIFT", "QK_L2NORM", "prefill_workspace_bytes", "chunk_prefill", "recurrent_verify",
     "commit", "commit_align", "state_copy", "conv_state_update", "LIB_PATH",
 ]
 
@@ -26,6 +26,7 @@ DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED",
           3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_LAUNCH"}
 DEV_ERR_SLOT, DEV_ERR_TRACK, DEV_ERR_ACCEPT, DEV_ERR_SEQLEN, DEV_ERR_SHIFT = 1, 2, 4, 8, 16
+QK_L2NORM = 1   # flags bit of kda_chunk_prefill / kda_recurrent_verify
 
 
 class KdaError(RuntimeError):
@@ -48,14 +49,15 @@ class KdaConvTensor(ctypes.Structure):
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
+_U32 = ctypes.c_uint32
 _SZ = ctypes.c_size_t
 
 _SIGS = {
     "kda_chunk_prefill_workspace": [_I32, _I64, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)],
     "kda_chunk_prefill": [_P, _P, _P, _P, _P, _I32, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32,
-                          KdaPool, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P],
+                          KdaPool, _P, _P, _P, _P, _P, _I32, _P, _U32, _P, _P, _SZ, _P],
     "kda_recurrent_verify": [_P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, KdaPool,
-                             _P, _P, _P, _P, _P],
+                             _P, _P, _P, _U32, _P, _P],
     "kda_commit": [KdaPool, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P],
     "kda_commit_align": [KdaPool, _P, _I32, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                          _P, _P],
@@ -126,9 +128,10 @@ def prefill_workspace_bytes(n_seqs, total_tokens, H, d_k, d_v, chunk, in_dtype):
 
 def chunk_prefill(q, k, v, g, b, cu_seqlens, chunk, pool, init_slot, final_slot,
                   track_ptr=None, track_chunk=None, track_slot=None, track_f32=None,
-                  o=None, dev_err=None, workspace=None):
+                  o=None, dev_err=None, workspace=None, qk_l2norm=False):
     """kda_chunk_prefill on packed token tensors q, k, g [T, H, d_k], v [T, H, d_v],
-    b [T, H]; returns o [T, H, d_v] (allocated when not given)."""
+    b [T, H]; returns o [T, H, d_v] (allocated when not given).  qk_l2norm sets
+    KDA_QK_L2NORM (q and k normalised per row inside the kernel)."""
     T, H, dk = q.shape
     dv = v.shape[2]
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("b", b)):
@@ -151,14 +154,16 @@ def chunk_prefill(q, k, v, g, b, cu_seqlens, chunk, pool, init_slot, final_slot,
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), DTYPE_CODES[q.dtype], _ptr(o),
         _ptr(cu_seqlens), n_seqs, T, H, dk, dv, chunk, _pool(pool), _ptr(init_slot),
         _ptr(final_slot), _ptr(track_ptr), _ptr(track_chunk), _ptr(track_slot), n_track,
-        _ptr(track_f32), _ptr(dev_err), _ptr(workspace), workspace.numel(), _stream())
+        _ptr(track_f32), QK_L2NORM if qk_l2norm else 0, _ptr(dev_err), _ptr(workspace),
+        workspace.numel(), _stream())
     _check(st, "kda_chunk_prefill")
     return o
 
 
-def recurrent_verify(q, k, v, g, b, pool, ckpt_slot, o=None, u_rec=None, kg_rec=None, dev_err=None):
+def recurrent_verify(q, k, v, g, b, pool, ckpt_slot, o=None, u_rec=None, kg_rec=None, dev_err=None,
+                     qk_l2norm=False):
     """kda_recurrent_verify on q, k, g [n_req, L, H, d_k], v [n_req, L, H, d_v],
-    b [n_req, L, H]; returns (o, u_rec, kg_rec)."""
+    b [n_req, L, H]; returns (o, u_rec, kg_rec).  qk_l2norm as in chunk_prefill."""
     n_req, L, H, dk = q.shape
     dv = v.shape[3]
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("b", b)):
@@ -176,7 +181,8 @@ def recurrent_verify(q, k, v, g, b, pool, ckpt_slot, o=None, u_rec=None, kg_rec=
     _dev(kg_rec, "kg_rec", dtype=q.dtype)
     st = lib().kda_recurrent_verify(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), DTYPE_CODES[q.dtype], _ptr(o), n_req, L, H,
-        dk, dv, _pool(pool), _ptr(ckpt_slot), _ptr(u_rec), _ptr(kg_rec), _ptr(dev_err), _stream())
+        dk, dv, _pool(pool), _ptr(ckpt_slot), _ptr(u_rec), _ptr(kg_rec), QK_L2NORM if qk_l2norm else 0,
+        _ptr(dev_err), _stream())
     _check(st, "kda_recurrent_verify")
     return o, u_rec, kg_rec
 

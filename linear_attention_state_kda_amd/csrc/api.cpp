@@ -62,11 +62,13 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
                              const int32_t* init_slot, const int32_t* final_slot,
                              const int32_t* track_ptr, const int32_t* track_chunk,
                              const int32_t* track_slot, int32_t n_track, float* track_f32,
-                             int32_t* dev_err, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+                             uint32_t flags, int32_t* dev_err, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   if (n_seqs < 0 || total_tokens < 0 || H <= 0 || n_track < 0) return KDA_ERR_INVALID_ARG;
+  if ((flags & ~KDA_QK_L2NORM) != 0) return KDA_ERR_INVALID_ARG;
   if (!dtype_ok(in_dtype)) return KDA_ERR_UNSUPPORTED;
   if (!kda::prefill_supported(d_k, d_v, chunk, in_dtype, pool.dtype)) return KDA_ERR_UNSUPPORTED;
+  if ((flags & KDA_QK_L2NORM) && d_k != 128) return KDA_ERR_UNSUPPORTED;   // 16-bit path only
   if (total_tokens > INT32_MAX) return KDA_ERR_UNSUPPORTED;
   kda_status ps = check_pool(pool, H, d_k, d_v);
   if (ps != KDA_OK) return ps;
@@ -86,7 +88,7 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
   kda::PrefillArgs a{q, k, v, g, b, o, in_dtype, cu_seqlens, n_seqs, total_tokens, H, d_k, d_v,
                      chunk, pool_desc(pool), init_slot, final_slot,
                      n_track > 0 ? track_ptr : nullptr, track_chunk, track_slot, n_track,
-                     track_f32, dev_err, workspace};
+                     track_f32, dev_err, workspace, flags};
   return launched(kda::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -94,8 +96,9 @@ kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, con
                                 const void* b, int32_t in_dtype, void* o, int32_t n_req,
                                 int32_t L, int32_t H, int32_t d_k, int32_t d_v, kda_pool pool,
                                 const int32_t* ckpt_slot, float* u_rec, void* kg_rec,
-                                int32_t* dev_err, void* stream) {
+                                uint32_t flags, int32_t* dev_err, void* stream) {
   if (n_req < 0 || H <= 0 || L < 1) return KDA_ERR_INVALID_ARG;
+  if ((flags & ~KDA_QK_L2NORM) != 0) return KDA_ERR_INVALID_ARG;
   if (L > 256) return KDA_ERR_UNSUPPORTED;
   if (!dtype_ok(in_dtype)) return KDA_ERR_UNSUPPORTED;
   if (d_k != 128 || d_v != 128) return KDA_ERR_UNSUPPORTED;
@@ -110,7 +113,7 @@ kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, con
     return KDA_ERR_INVALID_ARG;
   if ((int64_t)n_req * H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
   kda::VerifyArgs a{q, k, v, g, b, o, in_dtype, n_req, L, H, d_k, pool_desc(pool), ckpt_slot,
-                    u_rec, kg_rec, dev_err};
+                    u_rec, kg_rec, dev_err, flags};
   return launched(kda::launch_verify(a, static_cast<hipStream_t>(stream)));
 }
 

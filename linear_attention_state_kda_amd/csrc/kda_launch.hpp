@@ -31,6 +31,7 @@ struct PrefillArgs {
   float* track_f32;
   int32_t* dev_err;
   void* workspace;
+  uint32_t flags;   // KDA_QK_L2NORM
 };
 
 struct VerifyArgs {
@@ -43,6 +44,7 @@ struct VerifyArgs {
   float* u_rec;
   void* kg_rec;
   int32_t* dev_err;
+  uint32_t flags;   // KDA_QK_L2NORM
 };
 
 struct CommitArgs {

@@ -143,7 +143,7 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void kda_chunk_prep16(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ g,
     const T* __restrict__ bl, const int32_t* __restrict__ cu, int n_seqs, int64_t total,
-    int H, int64_t cap, const int32_t* __restrict__ off, uint8_t* __restrict__ recs) {
+    int H, int64_t cap, const int32_t* __restrict__ off, uint8_t* __restrict__ recs, int l2norm) {
   constexpr int DK = 128, C = 64, NFK = DK / 32;
   typedef Rec16 R;
   typedef typename OpTraits<T>::frag F8;   // 8 x 16-bit fragment
@@ -209,6 +209,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   regroup(graw, grw);
   regroup(kraw, kr);
   regroup(qraw, qr);
+  // ---- optional L2 normalisation of the k and q rows: the four lanes
+  //      16 g + r (g = 0..3) hold token r's 128 channels; each row is scaled
+  //      by 1 / sqrt(sum x^2 + 1e-6) in fp32 and rounded once to T, so the
+  //      record holds what verify would see for the same token
+  if (l2norm) {
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NFK; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = to_f32(kr[kb][hf][e]), y = to_f32(qr[kb][hf][e]);
+          sk += x * x;
+          sq += y * y;
+        }
+    sk += __shfl_xor(sk, 16);
+    sq += __shfl_xor(sq, 16);
+    sk += __shfl_xor(sk, 32);
+    sq += __shfl_xor(sq, 32);
+    const float ks = rsqrtf(sk + 1e-6f), qs = rsqrtf(sq + 1e-6f);
+#pragma unroll
+    for (int kb = 0; kb < NFK; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kr[kb][hf][e] = from_f32<T>(to_f32(kr[kb][hf][e]) * ks);
+          qr[kb][hf][e] = from_f32<T>(to_f32(qr[kb][hf][e]) * qs);
+        }
+  }
   const float beta = valid ? sigmoidf_(to_f32(braw)) : 0.f;
   if (gq == 0) sm.beta[t] = beta;
 
@@ -808,7 +839,7 @@ hipError_t run16(const PrefillArgs& a, hipStream_t st, int64_t cap, const int32_
     hipLaunchKernelGGL(kda_chunk_prep16<TIn>, dim3((unsigned)(cap * a.H)), dim3(kThreads), 0, st,
                        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                        static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.b), a.cu_seqlens,
-                       a.n_seqs, a.total_tokens, a.H, cap, off, recs);
+                       a.n_seqs, a.total_tokens, a.H, cap, off, recs, (a.flags & 1u) ? 1 : 0);
   const int64_t pairs = (int64_t)a.n_seqs * a.H;
   const int64_t pairs8 = (pairs + kXcd - 1) / kXcd * kXcd;
   // Each workgroup streams its head's whole record per chunk through its

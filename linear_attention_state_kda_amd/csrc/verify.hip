@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(resident_wgs
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const TIn* __restrict__ g, const TIn* __restrict__ bl, TIn* __restrict__ o, int n_req, int L,
     int H, const TPool* __restrict__ pool, int64_t n_slots, const int32_t* __restrict__ ckpt,
-    float* __restrict__ u_rec, TIn* __restrict__ kg_rec, int32_t* __restrict__ dev_err) {
+    float* __restrict__ u_rec, TIn* __restrict__ kg_rec, int32_t* __restrict__ dev_err, int l2norm) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   constexpr int EP = 16 / (int)sizeof(TIn);   // input elements per 16-byte piece
   constexpr int PPR = kD / EP;                 // pieces per 128-element row
@@ -176,6 +176,25 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(resident_wgs
     }
     if (tid < kTB) s_beta[tid] = tid < nb ? sigmoidf_(to_f32(braw)) : 0.f;
     __syncthreads();
+    // ---- optional L2 normalisation of the block's k and q rows in place
+    //      (16 threads per row, 8 channels each), rounded once to the input
+    //      dtype: the recurrence and the key record both use the result
+    if (l2norm) {
+      const int rr = tid >> 4, a = rr < kTB ? 0 : 2, c0 = 8 * (tid & 15);
+      TIn* const rp = &s_stage[(a * kTB + (rr & (kTB - 1))) * kD + c0];
+      float x[8], ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        x[i] = to_f32(rp[i]);
+        ss += x[i] * x[i];
+      }
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) ss += __shfl_xor(ss, m);
+      const float sc = rsqrtf(ss + 1e-6f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rp[i] = from_f32<TIn>(x[i] * sc);
+      __syncthreads();
+    }
     // ---- per-position vectors: thread (key channel c, half hh) runs the
     //      cumulative decay over positions 4 hh .. 4 hh + 3 (the second half
     //      first runs it over positions 0..3); 1/D as a product of exp(-g)
@@ -345,7 +364,7 @@ hipError_t by_pool(const VerifyArgs& a, hipStream_t st) {
                      static_cast<const TIn*>(a.v), static_cast<const TIn*>(a.g),                   \
                      static_cast<const TIn*>(a.b), static_cast<TIn*>(a.o), a.n_req, a.L, a.H,      \
                      static_cast<const TP*>(a.pool.base), a.pool.n_slots, a.ckpt_slot, a.u_rec,    \
-                     static_cast<TIn*>(a.kg_rec), a.dev_err)
+                     static_cast<TIn*>(a.kg_rec), a.dev_err, (a.flags & 1u) ? 1 : 0)
   switch (a.pool.dtype) {
     case F32: KDA_VERIFY_LAUNCH(float); break;
     case F16: KDA_VERIFY_LAUNCH(f16); break;

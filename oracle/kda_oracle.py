@@ -49,7 +49,10 @@ Readings where the pages are silent (each is listed in the design doc):
   * the gate input is g = log alpha and alpha = exp(g) with no further
     activation; the beta input is a logit and every call applies the same
     sigmoid;
-  * no query scale and no q/k normalisation inside the recurrence;
+  * no query scale and no q/k normalisation inside the recurrence; where a
+    call normalises q and k itself (an optional flag), that is a
+    preprocessing step in front of it: ``l2norm_rows`` below, then one
+    rounding to the input dtype;
   * the snapshot at chunk index c is the state after c full chunks, i.e.
     after c*C tokens of that sequence, valid for 0 <= c <= floor(T_i / C);
   * accepted length n in [0, L] is the number of verified positions folded
@@ -65,6 +68,7 @@ import numpy as np
 
 __all__ = [
     "sigmoid",
+    "l2norm_rows",
     "kda_step",
     "run_sequence",
     "prefill_ref",
@@ -85,6 +89,18 @@ def sigmoid(x):
     x = np.asarray(x, dtype=np.float64)
     z = np.exp(-np.abs(x))
     return np.where(x >= 0, 1.0 / (1.0 + z), z / (1.0 + z))
+
+
+def l2norm_rows(x, eps=1e-6):
+    """x / sqrt(sum x^2 + eps) over the last axis, in float64.
+
+    The workloads normalise q and k per (token, head) over d_k ("q, k
+    L2-normalised per head"); the pages fix no epsilon, so eps = 1e-6 inside
+    the square root is a reading that only matters for rows of norm near
+    1e-3 or below (a zero row stays zero).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
 
 
 def kda_step(S, q_t, k_t, v_t, g_t, b_t):

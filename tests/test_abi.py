@@ -56,13 +56,14 @@ def pool(H=2, dk=128, dv=128, dtype=0, n_slots=8, base=FAKE):
 def prefill(L, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, in_dtype=2, o=FAKE, cu=FAKE, n_seqs=1,
              T=100, H=2, dk=128, dv=128, C=64, pool=pool(), init=FAKE, final=FAKE, tptr=None,
-             tchunk=None, tslot=None, n_track=0, tf32=None, err=None, ws=FAKE_WS,
+             tchunk=None, tslot=None, n_track=0, tf32=None, flags=0, err=None, ws=FAKE_WS,
              ws_bytes=1 << 40, stream=None)
     a.update(kw)
     return L.kda_chunk_prefill(a["q"], a["k"], a["v"], a["g"], a["b"], a["in_dtype"], a["o"],
                                a["cu"], a["n_seqs"], a["T"], a["H"], a["dk"], a["dv"], a["C"],
                                a["pool"], a["init"], a["final"], a["tptr"], a["tchunk"], a["tslot"],
-                               a["n_track"], a["tf32"], a["err"], a["ws"], a["ws_bytes"], a["stream"])
+                               a["n_track"], a["tf32"], a["flags"], a["err"], a["ws"], a["ws_bytes"],
+                               a["stream"])
 
 
 def test_prefill_host_errors(L):
@@ -83,6 +84,8 @@ def test_prefill_host_errors(L):
     assert prefill(L, ws=ctypes.c_void_p(0x100010)) == 3   # misaligned workspace
     assert prefill(L, q=ctypes.c_void_p(0x1002)) == 1       # misaligned input
     assert prefill(L, T=1 << 33) == 2
+    assert prefill(L, flags=2) == 1             # unknown flag bit
+    assert prefill(L, flags=1, in_dtype=0, dk=16, dv=16, C=16, pool=pool(dk=16, dv=16)) == 2
     # nothing to do: returns before touching anything
     assert prefill(L, n_seqs=0, q=None, cu=None) == 0
 
@@ -99,12 +102,13 @@ def test_workspace_query(L):
 
 def test_verify_commit_copy_host_errors(L):
     P = pool()
-    # verify: q, k, v, g, b, in_dtype, o, n_req, L, H, dk, dv, pool, ckpt, u, kg, err, stream
+    # verify: q, k, v, g, b, in_dtype, o, n_req, L, H, dk, dv, pool, ckpt, u, kg, flags, err, stream
     v = lambda **kw: L.kda_recurrent_verify(*[kw.get(n, d) for n, d in [
         ("q", FAKE), ("k", FAKE), ("v", FAKE), ("g", FAKE), ("b", FAKE), ("dt", 2), ("o", FAKE),
         ("n", 4), ("L", 8), ("H", 2), ("dk", 128), ("dv", 128), ("pool", P), ("ck", FAKE),
-        ("u", FAKE), ("kg", FAKE), ("err", None), ("st", None)]])
+        ("u", FAKE), ("kg", FAKE), ("fl", 0), ("err", None), ("st", None)]])
     assert v(L=0) == 1
+    assert v(fl=4) == 1
     assert v(L=257) == 2
     assert v(dk=64, dv=64) == 2
     assert v(o=None) == 1

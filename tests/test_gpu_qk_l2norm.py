@@ -1,0 +1,139 @@
+"""GPU parity of the fused q/k L2 normalisation (flags = KDA_QK_L2NORM).
+
+The workloads specify q and k "L2-normalised per head"; with the flag the
+prefill and verify kernels take q and k unnormalised and normalise each
+(token, head) row over d_k themselves, rounding the result once to the input
+dtype.  The oracle side is the same two steps on the CPU: ``l2norm_rows`` in
+fp64, one rounding to the input dtype, then the unchanged recurrence.
+
+Inputs: the seeded token rows of ``workloads.token_inputs`` with every q and
+k row scaled by its own factor in [0.3, 4] before rounding, so no row
+arrives normalised.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_state_kda_amd as kda
+import workloads as wl
+from oracle import kda_oracle as ko
+from tests.gpu_util import DEV, TOL, i32, make_pool, rel_per_head, to_math
+
+pytestmark = pytest.mark.gpu
+
+
+def raw_tokens(n_tokens, H, d, in_dtype, seed, shape_prefix=None):
+    toks = wl.token_inputs(n_tokens, H, d, d, in_dtype, seed, shape_prefix=shape_prefix)
+    rng = np.random.default_rng([seed, 99])
+    for n in "qk":
+        x = wl.exact(toks[n])
+        scale = rng.uniform(0.3, 4.0, size=x.shape[:-1] + (1,))
+        toks[n] = wl.to_dtype(x * scale, in_dtype)
+    return toks
+
+
+def normalised(toks, in_dtype):
+    """The oracle's view: q and k normalised in fp64, rounded once to in_dtype."""
+    ex = {n: wl.exact(toks[n]) for n in "qkvgb"}
+    for n in "qk":
+        ex[n] = wl.exact(wl.to_dtype(ko.l2norm_rows(ex[n]), in_dtype))
+    return ex
+
+
+@pytest.mark.parametrize("H,in_dtype", [(3, "bf16"), (12, "bf16"), (3, "f16")])
+def test_prefill_normalises_q_k(H, in_dtype):
+    lens = [300, 64, 1, 0, 130, 37]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, d, C = int(cu[-1]), 128, 64
+    toks = raw_tokens(T, H, d, in_dtype, seed=31)
+    n = len(lens)
+    pool = make_pool(2 * n, H, d, d, "f32")
+    init = [-1, 7, -1, 8, -1, 9]
+    S0 = np.zeros((n, H, d, d))
+    for i, s in enumerate(init):
+        if s >= 0:
+            pool[s] = wl.pool_state(s, H, d, d, "f32", 31).to(DEV)
+            S0[i] = to_math(pool[s])
+    tracks = [(0, 2, 10), (4, 1, 11)]
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    dev = {x: toks[x].to(DEV) for x in "qkvgb"}
+    o = kda.chunk_prefill(dev["q"], dev["k"], dev["v"], dev["g"], dev["b"], i32(cu), C, pool,
+                          i32(init), i32(list(range(n))), track_ptr=i32([0, 1, 1, 1, 1, 2, 2]),
+                          track_chunk=i32([2, 1]), track_slot=i32([10, 11]), dev_err=err,
+                          qk_l2norm=True)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ex = normalised(toks, in_dtype)
+    o_ref, fin_ref, snaps = ko.prefill_ref(ex["q"], ex["k"], ex["v"], ex["g"], ex["b"], cu, S0, C,
+                                           [(s, c) for s, c, _ in tracks])
+    tol = TOL[in_dtype]
+    og = wl.exact(o.cpu())
+    for i in range(n):
+        lo, hi = int(cu[i]), int(cu[i + 1])
+        if hi > lo:
+            assert rel_per_head(og[lo:hi], o_ref[lo:hi], 1) < tol
+        assert rel_per_head(to_math(pool[i]), fin_ref[i], 0) < tol
+    for e, (_, _, slot) in enumerate(tracks):
+        assert rel_per_head(to_math(pool[slot]), snaps[e], 0) < tol
+
+
+def test_prefill_flag_on_normalised_input_changes_little():
+    """Inputs already normalised (the workloads' own draw): the flag only
+    re-rounds, so outputs stay within the 16-bit bar of the flag-off run."""
+    case = wl.prefill_case([200, 77], 2, 128, 128, 64, "bf16", "f32", 4, [-1, -1], [0, 1], [], False,
+                           seed=32)
+    toks, cu = wl.prefill_tokens(case)
+    dev = {x: toks[x].to(DEV) for x in "qkvgb"}
+    outs = []
+    for flag in (False, True):
+        pool = make_pool(4, 2, 128, 128, "f32")
+        o = kda.chunk_prefill(dev["q"], dev["k"], dev["v"], dev["g"], dev["b"], i32(cu), 64, pool,
+                              i32([-1, -1]), i32([0, 1]), qk_l2norm=flag)
+        torch.cuda.synchronize()
+        outs.append(wl.exact(o.cpu()))
+    assert rel_per_head(outs[1], outs[0], 1) < 1e-2
+
+
+@pytest.mark.parametrize("L,in_dtype", [(8, "bf16"), (13, "bf16"), (8, "f16")])
+def test_verify_and_commit_normalise_q_k(L, in_dtype):
+    n_req, H, d = 6, 3, 128
+    toks = raw_tokens(n_req * L, H, d, in_dtype, seed=33, shape_prefix=(n_req, L))
+    ckpt = wl.distinct_slots(n_req, n_req + 2, 33)
+    pool = make_pool(n_req + 2, H, d, d, "f32")
+    for s in ckpt:
+        pool[int(s)] = wl.pool_state(int(s), H, d, d, "f32", 33).to(DEV)
+    S0 = np.stack([to_math(pool[int(s)]) for s in ckpt])
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    dev = {x: toks[x].to(DEV) for x in "qkvgb"}
+    o, u_rec, kg_rec = kda.recurrent_verify(dev["q"], dev["k"], dev["v"], dev["g"], dev["b"], pool,
+                                            i32(ckpt), dev_err=err, qk_l2norm=True)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ex = normalised(toks, in_dtype)
+    o_ref, u_ref, kg_ref, _ = ko.verify_ref(ex["q"], ex["k"], ex["v"], ex["g"], ex["b"], S0)
+    og, ug, kg = wl.exact(o.cpu()), u_rec.cpu().double().numpy(), wl.exact(kg_rec.cpu())
+    for i in range(n_req):
+        assert rel_per_head(og[i], o_ref[i], 1) < TOL[in_dtype]
+        # u is fp32 arithmetic, but a key that rounds to the neighbouring
+        # 16-bit value moves it by about 1e-4 relative
+        assert rel_per_head(ug[i], u_ref[i], 0) < 5e-3
+    # the key record holds the normalised key: equal to the oracle's rounding
+    # except where fp32 and fp64 normalisation round to neighbours (one ulp)
+    key, key_ref = kg[..., :d], kg_ref[..., :d]
+    mant = 7 if in_dtype == "bf16" else 10
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(key_ref), 1e-30))) - mant)
+    if in_dtype == "f16":
+        ulp = np.maximum(ulp, 2.0 ** -24)
+    assert np.all(np.abs(key - key_ref) <= ulp)
+    assert np.mean(key == key_ref) > 0.99
+    assert np.array_equal(kg[..., d:], kg_ref[..., d:])      # the raw gate is copied as is
+    # commit from those records = replay of the normalised tokens
+    acc = np.random.default_rng([33, 5]).integers(0, L + 1, n_req)
+    kda.commit(pool, i32(ckpt), i32(acc), u_rec, kg_rec, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    for i, s in enumerate(ckpt):
+        n = int(acc[i])
+        ref = ko.replay_ref(ex["q"][i], ex["k"][i], ex["v"][i], ex["g"][i], ex["b"][i], S0[i], n)
+        assert rel_per_head(to_math(pool[int(s)]), ref, 0) < 5e-3

@@ -357,3 +357,20 @@ def test_commit_pin_catches_forward_order_decay():
     replay = ko.replay_ref(q, k, v, g, b, S0, n)
     assert rel(right, replay) < 1e-13
     assert rel(wrong, replay) > 1e-3
+
+
+def test_l2norm_rows():
+    """q/k normalisation per (token, head) over d_k: a 3-4-5 row, unit norms,
+    the library norm, direction, scale invariance, a zero row."""
+    row = np.zeros(16)
+    row[:2] = (3.0, 4.0)
+    got = ko.l2norm_rows(row)
+    assert np.allclose(got[:2], (0.6, 0.8), rtol=3e-8, atol=0) and not got[2:].any()
+    x = np.random.default_rng(21).standard_normal((5, 3, 128)) * 4.0
+    y = ko.l2norm_rows(x)
+    assert np.allclose(np.sqrt((y * y).sum(-1)), 1.0, rtol=1e-9, atol=0)   # over d_k, per (token, head)
+    assert np.allclose(y, x / np.linalg.norm(x, axis=-1, keepdims=True), rtol=1e-9, atol=0)
+    assert np.allclose(y * np.linalg.norm(x, axis=-1, keepdims=True), x, rtol=1e-8, atol=0)
+    assert np.allclose(ko.l2norm_rows(7.5 * x), y, rtol=1e-9, atol=0)
+    z = ko.l2norm_rows(np.zeros((2, 128)))
+    assert np.array_equal(z, np.zeros((2, 128)))
