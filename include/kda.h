@@ -89,9 +89,7 @@ typedef enum { KDA_F32 = 0, KDA_F16 = 1, KDA_BF16 = 2 } kda_dtype;
  * commit from the records replays exactly what verify computed.  This is
  * the per-head L2 normalisation of q and k that the single-layer and
  * varlen workloads specify, fused into the loads instead of a separate
- * pass.  Built for the 16-bit (128, 128, 64) prefill and for verify; the
- * fp32 (16, 16, 16) prefill returns KDA_ERR_UNSUPPORTED with it.  Other
- * bits are rejected with KDA_ERR_INVALID_ARG. */
+ * pass.  Other bits are rejected with KDA_ERR_INVALID_ARG. */
 #define KDA_QK_L2NORM 1u
 
 /* Bits set in *dev_err by the kernels. */

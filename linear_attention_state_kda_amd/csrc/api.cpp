@@ -68,7 +68,6 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
   if ((flags & ~KDA_QK_L2NORM) != 0) return KDA_ERR_INVALID_ARG;
   if (!dtype_ok(in_dtype)) return KDA_ERR_UNSUPPORTED;
   if (!kda::prefill_supported(d_k, d_v, chunk, in_dtype, pool.dtype)) return KDA_ERR_UNSUPPORTED;
-  if ((flags & KDA_QK_L2NORM) && d_k != 128) return KDA_ERR_UNSUPPORTED;   // 16-bit path only
   if (total_tokens > INT32_MAX) return KDA_ERR_UNSUPPORTED;
   kda_status ps = check_pool(pool, H, d_k, d_v);
   if (ps != KDA_OK) return ps;

@@ -116,7 +116,7 @@ template <int DK, int C, typename TIn, typename TOp>
 __global__ __launch_bounds__(kThreads) void kda_chunk_prep(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ g,
     const TIn* __restrict__ bl, const int32_t* __restrict__ cu, int n_seqs, int64_t total,
-    int H, int64_t cap, const int32_t* __restrict__ off, uint8_t* __restrict__ recs) {
+    int H, int64_t cap, const int32_t* __restrict__ off, uint8_t* __restrict__ recs, int l2norm) {
   typedef PrepSmem<DK, C, TOp> Sm;
   typedef Rec<DK, C, TOp> R;
   constexpr int KBK = R::KBK, KBT = R::KBT;
@@ -177,6 +177,31 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_prep(
       gprod = gprod * alpha;
       fw[jj] = gprod;  // prod_{s <= t, s in group} alpha_s
       bw[jj] = alpha;  // temporarily alpha_t
+    }
+    // optional L2 normalisation of the k and q rows: the NCQ consecutive
+    // lanes cq = 0..NCQ-1 of a token group hold one row, 4 channels each;
+    // scaled by 1 / sqrt(sum x^2 + 1e-6) in fp32, rounded once to TIn
+    if (l2norm) {
+#pragma unroll
+      for (int jj = 0; jj < Sm::TPG; ++jj) {
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sk += kv[jj][e] * kv[jj][e];
+          sq += qv[jj][e] * qv[jj][e];
+        }
+#pragma unroll
+        for (int m = 1; m < Sm::NCQ; m <<= 1) {
+          sk += __shfl_xor(sk, m);
+          sq += __shfl_xor(sq, m);
+        }
+        const float ks = rsqrtf(sk + 1e-6f), qs = rsqrtf(sq + 1e-6f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kv[jj][e] = to_f32(from_f32<TIn>(kv[jj][e] * ks));
+          qv[jj][e] = to_f32(from_f32<TIn>(qv[jj][e] * qs));
+        }
+      }
     }
     // in-group suffix products: bw[jj] = prod_{jj < s < TPG} alpha_s
     floatx4 suf = {1.f, 1.f, 1.f, 1.f};
@@ -714,7 +739,7 @@ hipError_t run(const PrefillArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(kp, dim3((unsigned)(w.cap * a.H)), dim3(kThreads), smp, st,
                        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                        static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.b), a.cu_seqlens,
-                       a.n_seqs, a.total_tokens, a.H, w.cap, w.off, w.recs);
+                       a.n_seqs, a.total_tokens, a.H, w.cap, w.off, w.recs, (a.flags & 1u) ? 1 : 0);
   }
   auto ks = kda_chunk_scan<DK, DV, C, TIn, TOp, TPool>;
   const int64_t pairs = (int64_t)a.n_seqs * a.H;

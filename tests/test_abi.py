@@ -85,7 +85,6 @@ def test_prefill_host_errors(L):
     assert prefill(L, q=ctypes.c_void_p(0x1002)) == 1       # misaligned input
     assert prefill(L, T=1 << 33) == 2
     assert prefill(L, flags=2) == 1             # unknown flag bit
-    assert prefill(L, flags=1, in_dtype=0, dk=16, dv=16, C=16, pool=pool(dk=16, dv=16)) == 2
     # nothing to do: returns before touching anything
     assert prefill(L, n_seqs=0, q=None, cu=None) == 0
 

@@ -78,6 +78,31 @@ def test_prefill_normalises_q_k(H, in_dtype):
         assert rel_per_head(to_math(pool[slot]), snaps[e], 0) < tol
 
 
+def test_prefill_fp32_normalises_q_k():
+    """The fp32 configuration (d = 16, chunk 16): normalisation in fp32 is
+    held to the fp32 bar."""
+    lens = [64, 37, 16, 5]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, H, d, C = int(cu[-1]), 2, 16, 16
+    toks = raw_tokens(T, H, d, "f32", seed=34)
+    n = len(lens)
+    pool = make_pool(n, H, d, d, "f32")
+    dev = {x: toks[x].to(DEV) for x in "qkvgb"}
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    o = kda.chunk_prefill(dev["q"], dev["k"], dev["v"], dev["g"], dev["b"], i32(cu), C, pool,
+                          i32([-1] * n), i32(list(range(n))), dev_err=err, qk_l2norm=True)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ex = normalised(toks, "f32")
+    o_ref, fin_ref, _ = ko.prefill_ref(ex["q"], ex["k"], ex["v"], ex["g"], ex["b"], cu,
+                                       np.zeros((n, H, d, d)), C)
+    og = wl.exact(o.cpu())
+    for i in range(n):
+        lo, hi = int(cu[i]), int(cu[i + 1])
+        assert rel_per_head(og[lo:hi], o_ref[lo:hi], 1) < 1e-4
+        assert rel_per_head(to_math(pool[i]), fin_ref[i], 0) < 1e-4
+
+
 def test_prefill_flag_on_normalised_input_changes_little():
     """Inputs already normalised (the workloads' own draw): the flag only
     re-rounds, so outputs stay within the 16-bit bar of the flag-off run."""
