@@ -172,8 +172,9 @@ def test_small_multi_sequence(in_dtype, pool_dtype):
     print(in_dtype, pool_dtype, "worst rel", w)
 
 
-@pytest.mark.parametrize("H,pool_dtype", [(8, "f32"), (12, "bf16"), (12, "f32")])
-def test_wide_column_tiles(H, pool_dtype):
+@pytest.mark.parametrize("H,in_dtype,pool_dtype", [(8, "bf16", "f32"), (12, "bf16", "bf16"),
+                                                     (12, "bf16", "f32"), (12, "f16", "f16")])
+def test_wide_column_tiles(H, in_dtype, pool_dtype):
     """Enough (sequence, head) pairs that the scan takes wider column tiles:
     7 x 8 = 56 pairs (32-column tiles), 7 x 12 = 84 pairs (64-column tiles);
     every head checked against the oracle."""
@@ -181,12 +182,12 @@ def test_wide_column_tiles(H, pool_dtype):
     final = [0, 1, 2, 3, 4, 5, 6]
     tracks = [(0, 0, 7), (0, 2, 8), (0, 4, 9), (1, 1, 10), (4, 1, 11), (4, 2, 12), (5, 0, 13),
               (6, 2, 14), (6, 1, -1), (3, 0, 15)]
-    case = wl.prefill_case(SMALL_LENS, H, 128, 128, 64, "bf16", pool_dtype, 24, init, final,
+    case = wl.prefill_case(SMALL_LENS, H, 128, 128, 64, in_dtype, pool_dtype, 24, init, final,
                            tracks, True, seed=16)
     toks, cu = tokens(case)
     g = run_gpu(case, toks, cu)
     w = check_case(case, toks, cu, g, list(range(H)))
-    print("wide tiles H", H, pool_dtype, "worst rel", w)
+    print("wide tiles H", H, in_dtype, pool_dtype, "worst rel", w)
 
 
 def test_final_over_own_init_slot():
