@@ -685,7 +685,7 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan16(
     } else if (fs != -1 && lead && tid == 0) {
       set_err(dev_err, 1u);
     }
-  } else if (wv == 8) {
+  } else if (wv == 8 && nch > 0) {   // an empty sequence has no record to touch
     // ---- prefetch wave: lane l touches line l of share vt (one of NVT) of
     //      a record (lanes past the share or the record read nothing), and
     //      consumes each step's load two steps later
