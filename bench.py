@@ -8,9 +8,10 @@ One step = one pass of the whole path over resident synthetic inputs:
     workload (256 requests, L = 8, H = 32, fp32 128 x 128 checkpoints in a
     1024-slot pool, accepted ~ U{0..8}, in-place commit, fork of 64
     committed checkpoints to 4 children each).
-value = prefill tokens/s (T / mean prefill time).  An informational leg
-outside the step times the same prefill on the varlen batch (16 sequences,
-lengths ~ U[512, 16384]) and reports it as `prefill_varlen`.  Each call is
+value = prefill tokens/s (T / mean prefill time).  Informational legs
+outside the step time the same prefill on the varlen batch (16 sequences,
+lengths ~ U[512, 16384]; `prefill_varlen`) and on one 131072-token sequence
+(`prefill_long`).  Each call is
 bracketed by
 HIP events on the stream it is launched on; the roofline object covers the
 call that dominates the step.  The cpu_baseline leg times the fp64 oracle
@@ -118,13 +119,11 @@ def spec_setup(dev):
                            conv_fork=conv_op_bytes * n_fork))
 
 
-def varlen_setup(dev):
-    """The varlen prefill batch (16 packed sequences, lengths ~ U[512, 16384],
-    H = 32, d = 128, chunk 64, bf16 inputs, 1024-slot fp32 pool, initial
-    states from pool slots, one fp32 snapshot per sequence), drawn with torch's
-    generator on the device: the same distributions as the seeded workload,
-    without its fp64 host pass (this leg is timed, not checked)."""
-    case = wl.varlen_prefill("f32")
+def informational_setup(dev, case):
+    """A prefill workload for the informational legs, drawn with torch's
+    generator on the device: the same distributions as the seeded workload
+    (q, k unit rows, v, b ~ N(0, 1), g ~ U(-0.1, -0.001), pool states ~ N(0, 1)),
+    without its fp64 host pass (these legs are timed, not checked)."""
     lengths = np.asarray(case["lengths"], dtype=np.int64)
     T, H, d, C = int(lengths.sum()), case["H"], case["dk"], case["chunk"]
     gen = torch.Generator(device=dev).manual_seed(case["seed"])
@@ -149,10 +148,31 @@ def varlen_setup(dev):
                 o=torch.empty((T, H, d), dtype=torch.bfloat16, device=dev))
     args["workspace"] = torch.empty(kda.prefill_workspace_bytes(len(lengths), T, H, d, d, C, torch.bfloat16),
                                     dtype=torch.uint8, device=dev)
-    # per sequence-head: init read, final write, snapshot into the pool and the fp32 copy
-    bytes_ = T * H * (4 * d * 2 + 2 + d * 2) + len(lengths) * H * d * d * 4 * 4
+    # per sequence-head: init read (if any) and final write; per snapshot the
+    # pool write and the fp32 copy; all fp32
+    n_init = sum(1 for s_ in case["init_slots"] if s_ >= 0)
+    bytes_ = T * H * (4 * d * 2 + 2 + d * 2) + (n_init + len(lengths) + 2 * len(tr)) * H * d * d * 4
     flops = T * H * (6 * d * d + 5 * C * d)
     return args, T, len(lengths), bytes_, flops
+
+
+def time_leg(dev, st, case, label):
+    """Median of 5 prefill calls (after 2 untimed) on an informational workload."""
+    args, T, n, bytes_, flops = informational_setup(dev, case)
+    for _ in range(2):
+        kda.chunk_prefill(**args)
+    evs = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(5)]
+    for e0, e1 in evs:
+        e0.record(st)
+        kda.chunk_prefill(**args)
+        e1.record(st)
+    torch.cuda.synchronize()
+    ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+    del args
+    return {"workload": f"{label}, {n} sequence(s), {T} tokens, H=32, d=128, chunk 64, bf16, fp32 pool",
+            "ms_median": ms, "tokens_per_s": T / (ms * 1e-3),
+            "hbm_GBps": bytes_ / (ms * 1e-3) / 1e9, "hbm_frac": bytes_ / (ms * 1e-3) / HBM_PEAK,
+            "mfma_TFLOPs": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / BF16_PEAK}
 
 
 def measured_prefill_traffic():
@@ -205,7 +225,8 @@ def main():
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="extra steps, each after a 512 MiB cache-flushing write (0 to skip)")
     ap.add_argument("--no-varlen", action="store_true",
-                    help="skip the informational varlen prefill leg (16 sequences, 135k tokens)")
+                    help="skip the informational prefill legs (the varlen batch of 16 sequences "
+                         "and the long-context sequence of 131072 tokens)")
     ap.add_argument("--traffic-calibration", action="store_true",
                     help="after the timed steps, run one kda_state_copy of 256 distinct fp32 "
                          "slots (512 MiB read + 512 MiB written) so that FETCH_SIZE / WRITE_SIZE "
@@ -277,27 +298,16 @@ def main():
         cold = {c: np.array([cevs[s][i].elapsed_time(cevs[s][i + 1]) for s in range(a.cold_steps)])
                 for i, c in enumerate(calls)}
         del scratch
-    # Informational leg, outside the step and `value`: the same prefill
+    # Informational legs, outside the step and `value`: the same prefill
     # kernels on the varlen batch, where 16 sequences give the scan 16x more
-    # independent chains than the single-layer workload's one.
-    varlen = None
+    # independent chains than the single-layer workload's one, and on the
+    # long-context sequence (2048 serial chunks, a snapshot every 64).
+    varlen = long_ctx = None
     if not a.no_varlen:
-        vargs, vT, vn, vbytes, vflops = varlen_setup(dev)
-        for _ in range(2):
-            kda.chunk_prefill(**vargs)
-        vev = [[ev(), ev()] for _ in range(5)]
-        for e0, e1 in vev:
-            e0.record(st)
-            kda.chunk_prefill(**vargs)
-            e1.record(st)
-        torch.cuda.synchronize()
-        vms = float(np.median([e0.elapsed_time(e1) for e0, e1 in vev]))
-        varlen = {"workload": f"varlen prefill, {vn} sequences, {vT} tokens, H=32, d=128, chunk 64, "
-                              "bf16, fp32 pool, pool initial states, one snapshot per sequence",
-                  "ms_median": vms, "tokens_per_s": vT / (vms * 1e-3),
-                  "hbm_GBps": vbytes / (vms * 1e-3) / 1e9, "hbm_frac": vbytes / (vms * 1e-3) / HBM_PEAK,
-                  "mfma_TFLOPs": vflops / (vms * 1e-3) / 1e12, "mfma_frac": vflops / (vms * 1e-3) / BF16_PEAK}
-        del vargs
+        varlen = time_leg(dev, st, wl.varlen_prefill("f32"), "varlen prefill, pool initial states, "
+                                                              "one snapshot per sequence")
+        long_ctx = time_leg(dev, st, wl.long_prefill(), "long-context prefill, zero initial state, "
+                                                         "35 snapshots")
     if a.traffic_calibration:
         ck = sp["case"]["ckpt_slots"]
         fresh = sorted(set(range(sp["case"]["n_slots"])) - set(ck.tolist()))[:len(ck)]
@@ -367,6 +377,7 @@ def main():
                    "ms_p90": float(np.percentile(cold[c], 90))} for c in calls},
             "prefill_tokens_per_s": T / (float(np.median(cold["prefill"])) * 1e-3)},
         "prefill_varlen": varlen,
+        "prefill_long": long_ctx,
         "device": torch.cuda.get_device_name(0),
     }
     if not a.no_cpu_baseline:
