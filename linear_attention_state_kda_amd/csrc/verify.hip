@@ -57,11 +57,16 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Copy N bytes (4, 8 or 16; both addresses N-aligned) with one vector store.
+// Copy N bytes (4, 8 or 16; both addresses N-aligned) with one vector
+// store.  The outputs (o and the records) are stored non-temporally: the
+// next reader is another kernel, and dirty output lines left in the
+// memory-side cache slowed the next call's streaming reads (verify in a
+// verify / commit / copy loop 146 -> 143 us, commit reading the records
+// unchanged).
 template <int N, typename TD, typename TS>
 __device__ __forceinline__ void store_n(TD* dst, const TS* src) {
   typedef unsigned int vec __attribute__((ext_vector_type(N / 4)));
-  *reinterpret_cast<vec*>(dst) = *reinterpret_cast<const vec*>(src);
+  __builtin_nontemporal_store(*reinterpret_cast<const vec*>(src), reinterpret_cast<vec*>(dst));
 }
 
 // LDS writes of this wave visible to its other lanes
@@ -329,7 +334,7 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(resident_wgs
     //      ([position][k | g], contiguous): half vh writes positions
     //      4 vh .. 4 vh + 3.  u (fp32, contiguous per (req, head)) and o:
     //      this half's 64 columns.
-    *reinterpret_cast<kgvec*>(kg_rh + (int64_t)(t0 + jk) * (2 * kD) + ek) = kgv;
+    __builtin_nontemporal_store(kgv, reinterpret_cast<kgvec*>(kg_rh + (int64_t)(t0 + jk) * (2 * kD) + ek));
     {
       const int jj = min(tid / 32, nb - 1), c = (tid % 32) * 2;
       store_n<8>(u_rh + (int64_t)(t0 + jj) * kD + c, &s_u[jj][c]);
