@@ -4,6 +4,7 @@
 // risks item 1: a configuration the kernel cannot serve must fail at call
 // time, not inside the first step that hits it).
 #include <algorithm>
+#include <cstring>
 #include <hip/hip_runtime.h>
 
 #include "../../include/kda.h"
@@ -33,7 +34,11 @@ kda_status launched(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_LA
 
 extern "C" {
 
-const char* kda_status_string(kda_status s) {
+const char* kda_status_string(kda_status status) {
+  // Callers may pass any integer (a C enum is an int); read it as one, since
+  // loading an out-of-range value through the C++ enum type is undefined.
+  int32_t s;
+  std::memcpy(&s, &status, sizeof s);
   switch (s) {
     case KDA_OK: return "KDA_OK";
     case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG";
