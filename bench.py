@@ -194,6 +194,17 @@ def measured_prefill_traffic():
     return int(fields["traffic_bytes_per_call"])
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo when readable)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(case, seconds_target=20.0):
     """Time the fp64 oracle, single thread, on the first tokens of the prefill."""
     from threadpoolctl import threadpool_limits
@@ -382,7 +393,7 @@ def main():
     }
     if not a.no_cpu_baseline:
         cb = cpu_baseline(case)
-        cb["cpu"] = platform.processor() or platform.machine()
+        cb["cpu"] = cpu_model()
         out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 
