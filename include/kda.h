@@ -159,8 +159,10 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
  *   u_rec   [n_req][H][L][d_v] fp32 correction u_t (beta folded in),
  *   kg_rec  [n_req][H][L][2*d_k] in in_dtype: key k_t then raw gate g_t
  *           (with KDA_QK_L2NORM in flags, the normalised key).
+ * flags is 0 or KDA_QK_L2NORM (q and k normalised inside the kernel).
  * 1 <= L <= 256.  q, k, v, g, o, u_rec and kg_rec must be 16-byte aligned
- * (KDA_ERR_INVALID_ARG otherwise).  A request whose ckpt_slot is outside
+ * (KDA_ERR_INVALID_ARG otherwise).  The outputs are stored non-temporally
+ * (they are read by other kernels, not by this one).  A request whose ckpt_slot is outside
  * [0, n_slots) sets KDA_DEV_ERR_SLOT in *dev_err and its outputs are left
  * unwritten; the other requests are computed as usual. */
 kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, const void* g,
