@@ -190,12 +190,12 @@ def test_wide_column_tiles(H, in_dtype, pool_dtype):
     print("wide tiles H", H, in_dtype, pool_dtype, "worst rel", w)
 
 
-@pytest.mark.parametrize("H", [2, 12])
+@pytest.mark.parametrize("H", [2, 12, 16])
 def test_leading_empty_sequences(H):
     """Empty sequences first (chunk offset 0 on head 0): nothing of theirs is
     read from the workspace; their final state is the initial state cast
-    once; the sequences after them are unaffected.  H = 12 takes the wide
-    column tiles."""
+    once; the sequences after them are unaffected.  H = 12 and 16 take the
+    32- and 64-column tiles."""
     lens = [0, 0, 70, 0, 64]
     case = wl.prefill_case(lens, H, 128, 128, 64, "bf16", "f32", 12, [5, -1, 6, 7, -1],
                            [0, 1, 2, 3, 4], [(0, 0, 8), (2, 1, 9)], True, seed=17)
