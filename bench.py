@@ -11,8 +11,8 @@ One step = one pass of the whole path over resident synthetic inputs:
 value = prefill tokens/s (T / mean prefill time).  Informational legs
 outside the step time the same prefill on the varlen batch (16 sequences,
 lengths ~ U[512, 16384]; `prefill_varlen`) and on one 131072-token sequence
-(`prefill_long`).  Each call is
-bracketed by
+(`prefill_long`), and the verify -> commit -> fork copy loop of speculative
+decoding back to back (`decode_loop`).  Each call is bracketed by
 HIP events on the stream it is launched on; the roofline object covers the
 call that dominates the step.  The cpu_baseline leg times the fp64 oracle
 (single thread) on the first tokens of the same prefill workload.
@@ -175,6 +175,36 @@ def time_leg(dev, st, case, label):
             "mfma_TFLOPs": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / BF16_PEAK}
 
 
+def decode_loop_leg(sp, st, iters=10, warm=3):
+    """The speculative-decoding loop's own order on the speculative workload:
+    verify, in-place commit and fork copy, repeated back to back with no
+    synchronisation in between; per-call medians and roofline fractions."""
+    t = sp["t"]
+    names = ("verify", "commit", "copy")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(iters)]
+    for i in range(warm + iters):
+        e = evs[i - warm] if i >= warm else None
+        if e:
+            e[0].record(st)
+        kda.recurrent_verify(t["q"], t["k"], t["v"], t["g"], t["b"], sp["pool"], sp["ckpt"],
+                             o=sp["o"], u_rec=sp["u_rec"], kg_rec=sp["kg_rec"])
+        if e:
+            e[1].record(st)
+        kda.commit(sp["pool"], sp["ckpt"], sp["acc"], sp["u_rec"], sp["kg_rec"])
+        if e:
+            e[2].record(st)
+        kda.state_copy(sp["pool"], sp["src"], sp["dst"])
+        if e:
+            e[3].record(st)
+    torch.cuda.synchronize()
+    out = {"workload": "verify -> commit -> fork copy, repeated back to back (256 requests, L=8, "
+                       "H=32, fp32 pool), median of %d" % iters}
+    for j, c in enumerate(names):
+        ms = float(np.median([e[j].elapsed_time(e[j + 1]) for e in evs]))
+        out[c] = {"ms": round(ms, 4), "hbm_frac": round(sp["bytes"][c] / (ms * 1e-3) / HBM_PEAK, 4)}
+    return out
+
+
 def measured_prefill_traffic():
     """HBM bytes per prefill call from the committed FETCH_SIZE / WRITE_SIZE
     profile (already scaled by the copy calibration), or None when the
@@ -236,8 +266,9 @@ def main():
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="extra steps, each after a 512 MiB cache-flushing write (0 to skip)")
     ap.add_argument("--no-varlen", action="store_true",
-                    help="skip the informational prefill legs (the varlen batch of 16 sequences "
-                         "and the long-context sequence of 131072 tokens)")
+                    help="skip the informational legs (prefill on the varlen batch of 16 "
+                         "sequences and on the long-context sequence of 131072 tokens; the "
+                         "speculative-decoding loop)")
     ap.add_argument("--traffic-calibration", action="store_true",
                     help="after the timed steps, run one kda_state_copy of 256 distinct fp32 "
                          "slots (512 MiB read + 512 MiB written) so that FETCH_SIZE / WRITE_SIZE "
@@ -313,8 +344,9 @@ def main():
     # kernels on the varlen batch, where 16 sequences give the scan 16x more
     # independent chains than the single-layer workload's one, and on the
     # long-context sequence (2048 serial chunks, a snapshot every 64).
-    varlen = long_ctx = None
+    varlen = long_ctx = loop = None
     if not a.no_varlen:
+        loop = decode_loop_leg(sp, st)
         varlen = time_leg(dev, st, wl.varlen_prefill("f32"), "varlen prefill, pool initial states, "
                                                               "one snapshot per sequence")
         long_ctx = time_leg(dev, st, wl.long_prefill(), "long-context prefill, zero initial state, "
@@ -389,6 +421,7 @@ def main():
             "prefill_tokens_per_s": T / (float(np.median(cold["prefill"])) * 1e-3)},
         "prefill_varlen": varlen,
         "prefill_long": long_ctx,
+        "decode_loop": loop,
         "device": torch.cuda.get_device_name(0),
     }
     if not a.no_cpu_baseline:
