@@ -62,7 +62,7 @@ def prefill_setup(dev):
     args["o"] = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
     args["workspace"] = torch.empty(kda.prefill_workspace_bytes(1, T, H, d, d, C, torch.bfloat16),
                                     dtype=torch.uint8, device=dev)
-    # algorithmic traffic and work (see DESIGN.md): per token-head 4d+1 inputs
+    # algorithmic traffic and work: per token-head 4d+1 inputs
     # and d outputs in bf16; per sequence-head the zero init reads nothing, the
     # final state and one snapshot are written in fp32 plus the fp32 copy.
     bytes_ = T * H * (4 * d * 2 + 2 + d * 2) + H * d * d * 4 * 3

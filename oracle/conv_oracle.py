@@ -21,7 +21,7 @@ Sources (cited by page title and section):
   window (history plus the speculative positions), and after sampling the
   commit compacts the conv history to the accepted length.
 
-Layout and semantics (the readings this build adopts; the pages give the
+Layout and semantics (the readings adopted here; the pages give the
 operations, not a layout):
 
 * A conv tensor holds, per slot, a window of ``rows`` positions by ``dim``

@@ -45,7 +45,7 @@ S has shape (d_k, d_v) per head ("math orientation", key index first).  The
 GPU pool stores the transpose, [d_v][d_k] per head; converting between the
 two is the caller's job and is not part of the method.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * the gate input is g = log alpha and alpha = exp(g) with no further
     activation; the beta input is a logit and every call applies the same
     sigmoid;
@@ -291,7 +291,7 @@ ERR_SLOT, ERR_ACCEPT = 1, 4
 
 def commit_align_ref(slots, block_table, num_tokens, accepted, block_size, k_rec, g_rec, u_rec):
     """Align-mode RecoverSSM commit ([P3] Implementation breakdown steps 4-5
-    and the review's block-size check; the reading is this build's, the
+    and the review's block-size check; the reading is this library's, the
     pages give the commit plan only in outline).
 
     The state is kept per block of ``block_size`` tokens: the state after p
