@@ -88,17 +88,33 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _shape(t, name, shape):
+    """Raise ValueError unless tensor ``t`` (if given) has exactly ``shape``.
+    The C ABI sees raw pointers only, so every buffer size is checked here,
+    before any call: an undersized output would be written out of bounds."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)}, got {tuple(t.shape)}")
+
+
+def _same_device(ref, tensors):
+    for name, t in tensors:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
 def _dev(t, name, dtype=None, ndim=None):
     if t is None:
         return
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
 
 
 def _stream():
@@ -131,9 +147,33 @@ def chunk_prefill(q, k, v, g, b, cu_seqlens, chunk, pool, init_slot, final_slot,
                   o=None, dev_err=None, workspace=None, qk_l2norm=False):
     """kda_chunk_prefill on packed token tensors q, k, g [T, H, d_k], v [T, H, d_v],
     b [T, H]; returns o [T, H, d_v] (allocated when not given).  qk_l2norm sets
-    KDA_QK_L2NORM (q and k normalised per row inside the kernel)."""
+    KDA_QK_L2NORM (q and k normalised inside the kernel)."""
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q and v must be [T, H, d]")
     T, H, dk = q.shape
     dv = v.shape[2]
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-d tensor [n_seqs + 1]")
+    n_seqs = cu_seqlens.numel() - 1
+    if (track_chunk is None) != (track_slot is None) or (track_chunk is not None and track_ptr is None):
+        raise ValueError("track_ptr, track_chunk and track_slot go together")
+    n_track = 0 if track_chunk is None else track_chunk.numel()
+    _shape(k, "k", (T, H, dk))
+    _shape(g, "g", (T, H, dk))
+    _shape(v, "v", (T, H, dv))
+    _shape(b, "b", (T, H))
+    _shape(o, "o", (T, H, dv))
+    _shape(init_slot, "init_slot", (n_seqs,))
+    _shape(final_slot, "final_slot", (n_seqs,))
+    _shape(track_ptr, "track_ptr", (n_seqs + 1,))
+    _shape(track_chunk, "track_chunk", (n_track,))
+    _shape(track_slot, "track_slot", (n_track,))
+    if track_f32 is not None and (track_f32.dim() != 4 or tuple(track_f32.shape[1:]) != (H, dv, dk)
+                                  or track_f32.shape[0] < n_track):
+        raise ValueError(f"track_f32 must be [>= {n_track}, {H}, {dv}, {dk}], got {tuple(track_f32.shape)}")
+    if dev_err is not None and dev_err.numel() < 1:
+        raise ValueError("dev_err needs one element")
+    _shape(pool, "pool", (pool.shape[0], H, dv, dk))
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("b", b)):
         _dev(t, name, dtype=q.dtype)
     for name, t in (("cu_seqlens", cu_seqlens), ("init_slot", init_slot), ("final_slot", final_slot),
@@ -141,11 +181,13 @@ def chunk_prefill(q, k, v, g, b, cu_seqlens, chunk, pool, init_slot, final_slot,
                     ("dev_err", dev_err)):
         _dev(t, name, dtype=torch.int32)
     _dev(track_f32, "track_f32", dtype=torch.float32)
+    _same_device(q, (("k", k), ("v", v), ("g", g), ("b", b), ("o", o), ("pool", pool),
+                     ("cu_seqlens", cu_seqlens), ("init_slot", init_slot), ("final_slot", final_slot),
+                     ("track_ptr", track_ptr), ("track_chunk", track_chunk), ("track_slot", track_slot),
+                     ("track_f32", track_f32), ("dev_err", dev_err), ("workspace", workspace)))
     if o is None:
         o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
     _dev(o, "o", dtype=q.dtype)
-    n_seqs = cu_seqlens.numel() - 1
-    n_track = 0 if track_chunk is None else track_chunk.numel()
     need = prefill_workspace_bytes(n_seqs, T, H, dk, dv, chunk, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -164,12 +206,27 @@ def recurrent_verify(q, k, v, g, b, pool, ckpt_slot, o=None, u_rec=None, kg_rec=
                      qk_l2norm=False):
     """kda_recurrent_verify on q, k, g [n_req, L, H, d_k], v [n_req, L, H, d_v],
     b [n_req, L, H]; returns (o, u_rec, kg_rec).  qk_l2norm as in chunk_prefill."""
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q and v must be [n_req, L, H, d]")
     n_req, L, H, dk = q.shape
     dv = v.shape[3]
+    _shape(k, "k", (n_req, L, H, dk))
+    _shape(g, "g", (n_req, L, H, dk))
+    _shape(v, "v", (n_req, L, H, dv))
+    _shape(b, "b", (n_req, L, H))
+    _shape(o, "o", (n_req, L, H, dv))
+    _shape(u_rec, "u_rec", (n_req, H, L, dv))
+    _shape(kg_rec, "kg_rec", (n_req, H, L, 2 * dk))
+    _shape(ckpt_slot, "ckpt_slot", (n_req,))
+    _shape(pool, "pool", (pool.shape[0], H, dv, dk))
+    if dev_err is not None and dev_err.numel() < 1:
+        raise ValueError("dev_err needs one element")
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("b", b)):
         _dev(t, name, dtype=q.dtype)
     _dev(ckpt_slot, "ckpt_slot", dtype=torch.int32)
     _dev(dev_err, "dev_err", dtype=torch.int32)
+    _same_device(q, (("k", k), ("v", v), ("g", g), ("b", b), ("o", o), ("pool", pool),
+                     ("ckpt_slot", ckpt_slot), ("u_rec", u_rec), ("kg_rec", kg_rec), ("dev_err", dev_err)))
     if o is None:
         o = torch.empty((n_req, L, H, dv), dtype=q.dtype, device=q.device)
     if u_rec is None:
@@ -187,15 +244,35 @@ def recurrent_verify(q, k, v, g, b, pool, ckpt_slot, o=None, u_rec=None, kg_rec=
     return o, u_rec, kg_rec
 
 
+def _records(u_rec, kg_rec, pool):
+    """Sizes (n_req, H, L, d_k, d_v) of a verify call's records, checked
+    against each other and the pool."""
+    if u_rec.dim() != 4 or kg_rec.dim() != 4:
+        raise ValueError("u_rec and kg_rec must be 4-d [n_req, H, L, .]")
+    n_req, H, L, dv = u_rec.shape
+    if kg_rec.shape[3] % 2:
+        raise ValueError("kg_rec's last axis holds key then gate: 2 * d_k")
+    dk = kg_rec.shape[3] // 2
+    _shape(kg_rec, "kg_rec", (n_req, H, L, 2 * dk))
+    _shape(pool, "pool", (pool.shape[0], H, dv, dk))
+    return n_req, H, L, dk, dv
+
+
 def commit(pool, ckpt_slot, accepted_len, u_rec, kg_rec, dst_slot=None, dev_err=None):
     """kda_commit: rebuild each request's state at its accepted length."""
-    n_req, H, L, dv = u_rec.shape
-    dk = kg_rec.shape[3] // 2
+    n_req, H, L, dk, dv = _records(u_rec, kg_rec, pool)
+    _shape(ckpt_slot, "ckpt_slot", (n_req,))
+    _shape(accepted_len, "accepted_len", (n_req,))
+    _shape(dst_slot, "dst_slot", (n_req,))
+    if dev_err is not None and dev_err.numel() < 1:
+        raise ValueError("dev_err needs one element")
     for name, t in (("ckpt_slot", ckpt_slot), ("accepted_len", accepted_len), ("dst_slot", dst_slot),
                     ("dev_err", dev_err)):
         _dev(t, name, dtype=torch.int32)
     _dev(u_rec, "u_rec", dtype=torch.float32)
     _dev(kg_rec, "kg_rec")
+    _same_device(pool, (("ckpt_slot", ckpt_slot), ("accepted_len", accepted_len), ("dst_slot", dst_slot),
+                        ("u_rec", u_rec), ("kg_rec", kg_rec), ("dev_err", dev_err)))
     st = lib().kda_commit(_pool(pool), _ptr(ckpt_slot), _ptr(dst_slot), _ptr(accepted_len),
                           _ptr(u_rec), _ptr(kg_rec), DTYPE_CODES[kg_rec.dtype], n_req, L, H, dk,
                           dv, _ptr(dev_err), _stream())
@@ -204,15 +281,20 @@ def commit(pool, ckpt_slot, accepted_len, u_rec, kg_rec, dst_slot=None, dev_err=
 
 def commit_align(pool, block_table, num_tokens, accepted_len, block_size, u_rec, kg_rec, dev_err=None):
     """kda_commit_align: block-aligned commit; block_table is [n_req, blocks_per_req] int32."""
-    n_req, H, L, dv = u_rec.shape
-    dk = kg_rec.shape[3] // 2
+    n_req, H, L, dk, dv = _records(u_rec, kg_rec, pool)
+    if block_table.dim() != 2 or block_table.shape[0] != n_req:
+        raise ValueError(f"block_table must be [{n_req}, blocks_per_req], got {tuple(block_table.shape)}")
+    _shape(num_tokens, "num_tokens", (n_req,))
+    _shape(accepted_len, "accepted_len", (n_req,))
+    if dev_err is not None and dev_err.numel() < 1:
+        raise ValueError("dev_err needs one element")
     _dev(block_table, "block_table", dtype=torch.int32, ndim=2)
     for name, t in (("num_tokens", num_tokens), ("accepted_len", accepted_len), ("dev_err", dev_err)):
         _dev(t, name, dtype=torch.int32)
     _dev(u_rec, "u_rec", dtype=torch.float32)
     _dev(kg_rec, "kg_rec")
-    if block_table.shape[0] != n_req:
-        raise ValueError("block_table needs one row per request")
+    _same_device(pool, (("block_table", block_table), ("num_tokens", num_tokens),
+                        ("accepted_len", accepted_len), ("u_rec", u_rec), ("kg_rec", kg_rec), ("dev_err", dev_err)))
     st = lib().kda_commit_align(_pool(pool), _ptr(block_table), block_table.shape[1], _ptr(num_tokens),
                                 _ptr(accepted_len), int(block_size), _ptr(u_rec), _ptr(kg_rec),
                                 DTYPE_CODES[kg_rec.dtype], n_req, L, H, dk, dv, _ptr(dev_err), _stream())
@@ -221,11 +303,14 @@ def commit_align(pool, block_table, num_tokens, accepted_len, block_size, u_rec,
 
 def state_copy(pool, src_slot, dst_slot, dev_err=None):
     """kda_state_copy: pool[dst_slot[i]] <- pool[src_slot[i]] bitwise."""
+    if src_slot.dim() != 1 or dst_slot.dim() != 1 or src_slot.numel() != dst_slot.numel():
+        raise ValueError("src_slot and dst_slot must be 1-d tensors of one length")
+    if dev_err is not None and dev_err.numel() < 1:
+        raise ValueError("dev_err needs one element")
     _dev(src_slot, "src_slot", dtype=torch.int32)
     _dev(dst_slot, "dst_slot", dtype=torch.int32)
     _dev(dev_err, "dev_err", dtype=torch.int32)
-    if src_slot.numel() != dst_slot.numel():
-        raise ValueError("src_slot and dst_slot differ in length")
+    _same_device(pool, (("src_slot", src_slot), ("dst_slot", dst_slot), ("dev_err", dev_err)))
     st = lib().kda_state_copy(_pool(pool), _ptr(src_slot), _ptr(dst_slot), src_slot.numel(),
                               _ptr(dev_err), _stream())
     _check(st, "kda_state_copy")
@@ -248,11 +333,16 @@ def conv_state_update(tensors, keep, dst_slot, src_slot, shift, dev_err=None):
             raise ValueError("rows and channels of a conv tensor must be contiguous")
         descs[i] = KdaConvTensor(t.data_ptr(), t.stride(0) * t.element_size(), n_slots, rows, int(kp), dim,
                                  t.element_size())
-    for name, x in (("dst_slot", dst_slot), ("src_slot", src_slot), ("shift", shift), ("dev_err", dev_err)):
-        _dev(x, name, dtype=torch.int32)
     n = dst_slot.numel()
     if src_slot.numel() != n or shift.numel() != n:
         raise ValueError("dst_slot, src_slot and shift differ in length")
+    if dev_err is not None and dev_err.numel() < 1:
+        raise ValueError("dev_err needs one element")
+    for name, x in (("dst_slot", dst_slot), ("src_slot", src_slot), ("shift", shift), ("dev_err", dev_err)):
+        _dev(x, name, dtype=torch.int32)
+    if tensors:
+        _same_device(tensors[0], [(f"tensors[{i}]", t) for i, t in enumerate(tensors[1:], 1)] +
+                     [("dst_slot", dst_slot), ("src_slot", src_slot), ("shift", shift), ("dev_err", dev_err)])
     st = lib().kda_conv_state_update(descs, len(tensors), _ptr(dst_slot), _ptr(src_slot), _ptr(shift), n,
                                      _ptr(dev_err), _stream())
     _check(st, "kda_conv_state_update")

@@ -83,8 +83,9 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
     return KDA_ERR_INVALID_ARG;
   if (n_track > 0 && (track_ptr == nullptr || track_chunk == nullptr || track_slot == nullptr))
     return KDA_ERR_INVALID_ARG;
-  // 4-element vector loads of q, k, g and 16-byte stores of track_f32
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(g, 16) || !aligned(track_f32, 16))
+  // 16-byte vector loads of q, k, g and v, 16-byte stores of o and track_f32
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(g, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(track_f32, 16))
     return KDA_ERR_INVALID_ARG;
   const size_t need = kda::prefill_workspace_bytes(n_seqs, total_tokens, H, d_k, d_v, chunk, in_dtype);
   if (workspace == nullptr || workspace_bytes < need) return KDA_ERR_WORKSPACE;

@@ -77,6 +77,8 @@ __all__ = [
     "verify_ref",
     "replay_ref",
     "commit_ref",
+    "commit_align_ref",
+    "align_next_ref",
     "copy_ref",
 ]
 
@@ -340,6 +342,40 @@ def commit_align_ref(slots, block_table, num_tokens, accepted, block_size, k_rec
                 writes[s0] = commit_ref(S0, *rec, m)
             writes[s1] = commit_ref(S0, *rec, n)
     return writes, err
+
+
+def align_next_ref(block_table, num_tokens, accepted, block_size, L, n_slots):
+    """What the align-mode commit hands to the next step ([P3] Implementation
+    breakdown step 4: after the commit, the align post-processing moves each
+    request's running block index on and resets the next step's copy bias to
+    its neutral value).  Reading: per request r with p = num_tokens[r] and
+    n = accepted[r],
+      tokens  = p + n, the tokens the request holds after the commit;
+      block   = (p + n - 1) // block_size, the block of its last token,
+                whose slot now holds its current state;
+      ckpt    = block_table[r][block], the slot the next verify reads;
+      bias    = 0 (neutral: the state sits at the running block itself,
+                so the next step copies from no offset).
+    A request the commit skips (n outside [0, L]; p < 1; a block beyond its
+    table row; a slot outside [0, n_slots)) gets (p, -1, -1, 0).
+    Returns four int arrays (tokens, block, ckpt, bias).
+    """
+    n_req = len(num_tokens)
+    out = [np.zeros(n_req, dtype=np.int64) for _ in range(4)]
+    for r in range(n_req):
+        p, n = int(num_tokens[r]), int(accepted[r])
+        row = [int(x) for x in block_table[r]]
+        ok = 0 <= n <= L and p >= 1
+        if ok:
+            b0, b1 = (p - 1) // block_size, (p + n - 1) // block_size
+            ok = b1 < len(row) and all(0 <= row[b] < n_slots for b in (b0, b1))
+        if ok:
+            vals = (p + n, b1, row[b1], 0)
+        else:
+            vals = (p, -1, -1, 0)
+        for a, x in zip(out, vals):
+            a[r] = x
+    return tuple(out)
 
 
 def copy_ref(pool, src, dst):

@@ -44,6 +44,15 @@ int main(void) {
   expect("prefill chunk 32", PREFILL(fake, 1, 128, 32, KDA_BF16, 0u, (size_t)1 << 40), KDA_ERR_UNSUPPORTED);
   expect("prefill fp32 at d 128", PREFILL(fake, 1, 128, 64, KDA_F32, 0u, (size_t)1 << 40), KDA_ERR_UNSUPPORTED);
   expect("prefill small workspace", PREFILL(fake, 1, 128, 64, KDA_BF16, 0u, 16), KDA_ERR_WORKSPACE);
+  {
+    void* mis = (void*)(uintptr_t)0x100008;   /* 8-byte aligned only */
+    expect("prefill misaligned v", kda_chunk_prefill(fake, fake, mis, fake, fake, KDA_BF16, fake, fi, 1, 100, 2, 128, 128,
+                                                     64, pool, fi, fi, NULL, NULL, NULL, 0, NULL, 0u, NULL, fake_ws,
+                                                     (size_t)1 << 40, NULL), KDA_ERR_INVALID_ARG);
+    expect("prefill misaligned o", kda_chunk_prefill(fake, fake, fake, fake, fake, KDA_BF16, mis, fi, 1, 100, 2, 128, 128,
+                                                     64, pool, fi, fi, NULL, NULL, NULL, 0, NULL, 0u, NULL, fake_ws,
+                                                     (size_t)1 << 40, NULL), KDA_ERR_INVALID_ARG);
+  }
   expect("prefill nothing to do", PREFILL(NULL, 0, 128, 64, KDA_BF16, KDA_QK_L2NORM, 0), KDA_OK);
 #undef PREFILL
 

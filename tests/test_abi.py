@@ -82,7 +82,8 @@ def test_prefill_host_errors(L):
     assert prefill(L, ws_bytes=16) == 3
     assert prefill(L, ws=None) == 3
     assert prefill(L, ws=ctypes.c_void_p(0x100010)) == 3   # misaligned workspace
-    assert prefill(L, q=ctypes.c_void_p(0x1002)) == 1       # misaligned input
+    for name in ("q", "k", "v", "g", "o", "tf32"):   # every vector-accessed buffer must be 16-byte aligned
+        assert prefill(L, **{name: ctypes.c_void_p(0x1008)}) == 1, name
     assert prefill(L, T=1 << 33) == 2
     assert prefill(L, flags=2) == 1             # unknown flag bit
     # nothing to do: returns before touching anything

@@ -83,3 +83,55 @@ def test_matches_replay_for_every_offset(p):
             assert np.allclose(writes[100 + (p + n - 1) // BS], run, rtol=1e-12, atol=1e-12)
         else:
             assert writes == {}
+
+
+# (p, n) with BS = 5 -> (tokens, running block) worked from the block definition
+NEXT = [((2, 2), (4, 0)), ((3, 4), (7, 1)), ((5, 3), (8, 1)), ((4, 1), (5, 0)), ((7, 0), (7, 1)),
+        ((9, 4), (13, 2)), ((1, 0), (1, 0)), ((10, 0), (10, 1)), ((10, 1), (11, 2))]
+
+
+def test_next_step_literal_cases():
+    n_req = len(NEXT)
+    table = np.array([[10 * r + b + 1 for b in range(4)] for r in range(n_req)])
+    p = [c[0][0] for c in NEXT]
+    n = [c[0][1] for c in NEXT]
+    tokens, block, ckpt, bias = ko.align_next_ref(table, p, n, BS, L, n_slots=1000)
+    for r, (_, (t, b)) in enumerate(NEXT):
+        assert (tokens[r], block[r], ckpt[r], bias[r]) == (t, b, table[r][b], 0), r
+
+
+def test_next_step_errors():
+    table = np.array([[0, 1], [2, 3], [4, 5], [6, 99]])
+    # n > L; p = 0; a block beyond the row; a slot outside the pool (n_slots = 8)
+    tokens, block, ckpt, bias = ko.align_next_ref(table, [3, 0, 9, 7], [L + 1, 1, 2, 1], BS, L, n_slots=8)
+    assert list(tokens) == [3, 0, 9, 7]
+    assert list(block) == [-1] * 4 and list(ckpt) == [-1] * 4 and list(bias) == [0] * 4
+
+
+def test_next_step_chains_to_replay():
+    """Two align steps, the second from the first's running block: the state
+    the second writes at its running block is the replay of both windows."""
+    ex, S0, k_rec, g_rec, u_rec = case(1, 50)
+    table = np.array([[200, 201, 202, 203]])
+    p, n1 = 3, 4                                     # tokens 4..7: closes block 0, opens block 1
+    slots = {s: np.full((H, D, D), np.nan) for s in table[0]}
+    slots[200] = S0[0]
+    w1, err = ko.commit_align_ref(slots, table, [p], [n1], BS, k_rec, g_rec, u_rec)
+    assert err == 0
+    t1, b1, c1, _ = ko.align_next_ref(table, [p], [n1], BS, L, n_slots=1000)
+    assert (t1[0], b1[0], c1[0]) == (7, 1, 201)
+    slots.update(w1)
+    # second window: the next tokens of the same stream, verified from slot c1
+    toks2 = wl.token_inputs(L, H, D, D, "f32", 51, shape_prefix=(1, L))
+    ex2 = {x: wl.exact(toks2[x]) for x in "qkvgb"}
+    _, u2, kg2, _ = ko.verify_ref(ex2["q"], ex2["k"], ex2["v"], ex2["g"], ex2["b"], slots[int(c1[0])][None])
+    n2 = 4                                           # tokens 8..11: closes block 1 at 10, opens block 2
+    w2, err = ko.commit_align_ref(slots, table, [int(t1[0])], [n2], BS, kg2[..., :D], kg2[..., D:], u2)
+    assert err == 0
+    t2, b2, c2, _ = ko.align_next_ref(table, [int(t1[0])], [n2], BS, L, n_slots=1000)
+    assert (t2[0], b2[0], c2[0]) == (11, 2, 202)
+    whole = {x: np.concatenate([ex[x][0][:n1], ex2[x][0][:n2]]) for x in "qkvgb"}
+    rep = ko.replay_ref(*(whole[x] for x in "qkvgb"), S0[0], n1 + n2)
+    assert np.allclose(w2[int(c2[0])], rep, rtol=1e-12, atol=1e-12)
+    rep10 = ko.replay_ref(*(whole[x] for x in "qkvgb"), S0[0], 10 - p)   # block 1 ends at token 10
+    assert np.allclose(w2[201], rep10, rtol=1e-12, atol=1e-12)

@@ -10,7 +10,7 @@ import torch
 import linear_attention_state_kda_amd as kda
 import workloads as wl
 from oracle import kda_oracle as ko
-from tests.gpu_util import DEV, i32, make_pool, rel_per_head, to_math
+from tests.gpu_util import DEV, Worst, i32, make_pool, to_math
 
 pytestmark = pytest.mark.gpu
 
@@ -60,13 +60,14 @@ def test_commit_align_matches_oracle(pool_dtype, block_size):
     n = [8, 5, 1, 3, 0, 8, 8, 2, 8, 6]
     r = run_case(pool_dtype, bs, p, n)
     assert r["err"] == 0 and r["want_err"] == 0
-    tol = 1e-4 if pool_dtype == "f32" else 2e-2
+    w = Worst(1e-4 if pool_dtype == "f32" else 2e-2)
     written = set(r["writes"])
     for slot in range(r["pool"].shape[0]):
         if slot in written:
-            assert rel_per_head(to_math(r["pool"][slot]), r["writes"][slot], 0) < tol, slot
+            w.state("state", to_math(r["pool"][slot]), r["writes"][slot])
         else:
             assert torch.equal(r["pool"][slot], r["before"][slot]), slot
+    w.check(f"commit_align pool={pool_dtype} block={bs}")
 
 
 def test_commit_align_states_are_replays():
@@ -76,6 +77,7 @@ def test_commit_align_states_are_replays():
     p, n = [7, 9, 3], [5, 4, 6]
     r = run_case("f32", bs, p, n, seed=62)
     ex = {x: wl.exact(r["toks"][x]) for x in "qkvgb"}
+    w = Worst(1e-4)
     for i in range(len(p)):
         for j in range(1, n[i] + 1):
             t = p[i] + j                                   # 1-based token index
@@ -84,7 +86,8 @@ def test_commit_align_states_are_replays():
                 continue
             slot = int(r["table"][i][(t - 1) // bs])
             rep = ko.replay_ref(*(ex[x][i] for x in "qkvgb"), r["S0"][i], j)
-            assert rel_per_head(to_math(r["pool"][slot]), rep, 0) < 2e-2
+            w.state("replay", to_math(r["pool"][slot]), rep)
+    w.check("commit_align vs replays")
 
 
 def test_commit_align_errors():
@@ -109,8 +112,10 @@ def test_commit_align_short_window():
     r = run_case("f32", bs, p, n, L=L, seed=64)
     assert r["err"] == 0 and r["want_err"] == 0
     written = set(r["writes"])
+    w = Worst(1e-4)
     for slot in range(r["pool"].shape[0]):
         if slot in written:
-            assert rel_per_head(to_math(r["pool"][slot]), r["writes"][slot], 0) < 1e-4, slot
+            w.state("state", to_math(r["pool"][slot]), r["writes"][slot])
         else:
             assert torch.equal(r["pool"][slot], r["before"][slot]), slot
+    w.check("commit_align L=3 block 4")

@@ -12,7 +12,10 @@ kernel-level part of the replay-consistency question (state-semantics page,
 sec. 4 and the closing to-do list): the chunk kernel and the recurrent
 kernel take different floating-point paths, so the test reports their
 difference and bounds both against the fp64 oracle (2e-2 relative).
-The oracle runs on two sampled heads.
+The oracle runs on two sampled heads over the whole sequence, and on all 32
+heads over three 4096-token windows, each started from the kernel's own fp32
+snapshot at the window's start and compared row by row (outputs) and with the
+next snapshot.
 """
 
 import numpy as np
@@ -22,7 +25,7 @@ import torch
 import linear_attention_state_kda_amd as kda
 import workloads as wl
 from oracle import kda_oracle as ko
-from tests.gpu_util import DEV, i32, make_pool, rel_per_head, to_math
+from tests.gpu_util import DEV, Worst, i32, make_pool, rel_per_head, to_math
 
 pytestmark = pytest.mark.gpu
 
@@ -64,6 +67,23 @@ def test_long_context_prefill_and_replay():
         assert torch.equal(pool[slot], track_f32[e])        # fp32 pool: the cast is exact
     assert worst_snap < 2e-2
     assert rel_per_head(to_math(pool[case["final_slots"][0]][hsel]), S_T, 0) < 2e-2
+    w = Worst(2e-2)
+    w.out("o", o_gpu, o_ref, 1)
+    w.state("final", to_math(pool[case["final_slots"][0]][hsel]), S_T)
+    w.check("long T=131072 heads 0,17 whole sequence")
+
+    # ---- all heads on three 4096-token windows, each from the kernel's fp32
+    #      snapshot at its start: outputs row by row and the next snapshot
+    e_of = {c: e for e, (_, c, _) in enumerate(tracks)}
+    for m in (1, 16, 31):
+        lo, hi = 4096 * m, 4096 * (m + 1)
+        S_start = to_math(track_f32[e_of[64 * m]])
+        exw = {n: wl.exact(toks[n][lo:hi]) for n in "qkvgb"}
+        o_w, _, S_w, _ = ko.run_sequence(exw["q"], exw["k"], exw["v"], exw["g"], exw["b"], S_start)
+        ww = Worst(2e-2)
+        ww.out("o", wl.exact(o[lo:hi].cpu()), o_w, 1)
+        ww.state("snap", to_math(track_f32[e_of[64 * (m + 1)]]), S_w)
+        ww.check(f"long T=131072 all heads, tokens [{lo}, {hi}) from the fp32 snapshot c={64 * m}")
 
     # ---- replay: verify 256 tokens from snapshot 64 m, commit, compare with anchor 64 m + 4
     L = 256
@@ -79,6 +99,7 @@ def test_long_context_prefill_and_replay():
     torch.cuda.synchronize()
     assert err.item() == 0
     report = []
+    wr = Worst(2e-2)
     for i, m in enumerate(ms):
         s = starts[i]
         anchor = to_math(pool[slot_of[64 * m + 4]][hsel])
@@ -93,4 +114,8 @@ def test_long_context_prefill_and_replay():
         assert rel_per_head(vo_h, o_ref[s:s + L], 1) < 2e-2
         assert rel_per_head(vo_h, o_gpu[s:s + L], 1) < 2e-2
         report.append((m, diff, rel_per_head(committed, oracle_state, 0), rel_per_head(anchor, oracle_state, 0)))
+        wr.state("committed", committed, oracle_state)
+        wr.state("anchor", anchor, oracle_state)
+        wr.out("verify_o", vo_h, o_ref[s:s + L], 1)
+    wr.check("long T=131072 replay: verify+commit of 256 tokens vs oracle, heads 0,17")
     print("replay (m, |recurrent-chunked|, recurrent vs oracle, chunked vs oracle):", report)

@@ -18,7 +18,7 @@ import torch
 import linear_attention_state_kda_amd as kda
 import workloads as wl
 from oracle import kda_oracle as ko
-from tests.gpu_util import DEV, TOL, i32, make_pool, rel_per_head, to_math
+from tests.gpu_util import DEV, TOL, Worst, i32, make_pool, rel_per_head, to_math
 
 pytestmark = pytest.mark.gpu
 
@@ -67,15 +67,16 @@ def test_prefill_normalises_q_k(H, in_dtype):
     ex = normalised(toks, in_dtype)
     o_ref, fin_ref, snaps = ko.prefill_ref(ex["q"], ex["k"], ex["v"], ex["g"], ex["b"], cu, S0, C,
                                            [(s, c) for s, c, _ in tracks])
-    tol = TOL[in_dtype]
+    w = Worst(TOL[in_dtype])
     og = wl.exact(o.cpu())
     for i in range(n):
         lo, hi = int(cu[i]), int(cu[i + 1])
         if hi > lo:
-            assert rel_per_head(og[lo:hi], o_ref[lo:hi], 1) < tol
-        assert rel_per_head(to_math(pool[i]), fin_ref[i], 0) < tol
+            w.out("o", og[lo:hi], o_ref[lo:hi], 1)
+        w.state("final", to_math(pool[i]), fin_ref[i])
     for e, (_, _, slot) in enumerate(tracks):
-        assert rel_per_head(to_math(pool[slot]), snaps[e], 0) < tol
+        w.state("snap", to_math(pool[slot]), snaps[e])
+    w.check(f"prefill l2norm H={H} {in_dtype}")
 
 
 def test_prefill_fp32_normalises_q_k():
@@ -97,10 +98,12 @@ def test_prefill_fp32_normalises_q_k():
     o_ref, fin_ref, _ = ko.prefill_ref(ex["q"], ex["k"], ex["v"], ex["g"], ex["b"], cu,
                                        np.zeros((n, H, d, d)), C)
     og = wl.exact(o.cpu())
+    w = Worst(1e-4)
     for i in range(n):
         lo, hi = int(cu[i]), int(cu[i + 1])
-        assert rel_per_head(og[lo:hi], o_ref[lo:hi], 1) < 1e-4
-        assert rel_per_head(to_math(pool[i]), fin_ref[i], 0) < 1e-4
+        w.out("o", og[lo:hi], o_ref[lo:hi], 1)
+        w.state("final", to_math(pool[i]), fin_ref[i])
+    w.check("prefill l2norm fp32 d=16")
 
 
 def test_prefill_flag_on_normalised_input_changes_little():
@@ -136,16 +139,11 @@ def test_verify_and_commit_normalise_q_k(L, in_dtype):
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     ex = normalised(toks, in_dtype)
-    o_ref, u_ref, kg_ref, _ = ko.verify_ref(ex["q"], ex["k"], ex["v"], ex["g"], ex["b"], S0)
-    og, ug, kg = wl.exact(o.cpu()), u_rec.cpu().double().numpy(), wl.exact(kg_rec.cpu())
-    for i in range(n_req):
-        assert rel_per_head(og[i], o_ref[i], 1) < TOL[in_dtype]
-        # u is fp32 arithmetic, but a key that rounds to the neighbouring
-        # 16-bit value moves it by about 1e-4 relative
-        assert rel_per_head(ug[i], u_ref[i], 0) < 5e-3
+    kg = wl.exact(kg_rec.cpu())
     # the key record holds the normalised key: equal to the oracle's rounding
     # except where fp32 and fp64 normalisation round to neighbours (one ulp)
-    key, key_ref = kg[..., :d], kg_ref[..., :d]
+    key = kg[..., :d]
+    key_ref = np.transpose(ex["k"], (0, 2, 1, 3))
     mant = {"bf16": 7, "f16": 10, "f32": 23}[in_dtype]
     ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(key_ref), 1e-30))) - mant)
     if in_dtype == "f16":
@@ -157,13 +155,29 @@ def test_verify_and_commit_normalise_q_k(L, in_dtype):
     else:
         assert np.all(np.abs(key - key_ref) <= ulp)
         assert np.mean(key == key_ref) > 0.99
-    assert np.array_equal(kg[..., d:], kg_ref[..., d:])      # the raw gate is copied as is
+    assert np.array_equal(kg[..., d:], np.transpose(ex["g"], (0, 2, 1, 3)))   # the raw gate as is
+    # Where a 16-bit key rounds to the neighbouring value the recurrence is
+    # that of the kernel's key, so the oracle takes the key from the record
+    # (checked just above against l2norm_rows); u and the commit are then
+    # fp32 arithmetic on exact inputs and are held to the fp32 bar.  (With
+    # fp32 inputs the two keys differ by a few fp32 ulp only.)
+    ex["k"] = np.transpose(key, (0, 2, 1, 3))
+    o_ref, u_ref, kg_ref, _ = ko.verify_ref(ex["q"], ex["k"], ex["v"], ex["g"], ex["b"], S0)
+    og, ug = wl.exact(o.cpu()), u_rec.cpu().double().numpy()
+    wo, wu = Worst(TOL[in_dtype]), Worst(1e-4)
+    for i in range(n_req):
+        wo.out("o", og[i], o_ref[i], 1)
+        wu.out("u", ug[i], u_ref[i], 0)
+    wo.check(f"verify l2norm {in_dtype} L={L} o")
+    wu.check(f"verify l2norm {in_dtype} L={L} u")
     # commit from those records = replay of the normalised tokens
     acc = np.random.default_rng([33, 5]).integers(0, L + 1, n_req)
     kda.commit(pool, i32(ckpt), i32(acc), u_rec, kg_rec, dev_err=err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
+    wc = Worst(1e-4)
     for i, s in enumerate(ckpt):
         n = int(acc[i])
         ref = ko.replay_ref(ex["q"][i], ex["k"][i], ex["v"][i], ex["g"][i], ex["b"][i], S0[i], n)
-        assert rel_per_head(to_math(pool[int(s)]), ref, 0) < 5e-3
+        wc.state("commit", to_math(pool[int(s)]), ref)
+    wc.check(f"commit l2norm {in_dtype} L={L}")

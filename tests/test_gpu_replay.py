@@ -17,7 +17,7 @@ import torch
 import replay
 import workloads as wl
 from oracle import kda_oracle as ko
-from tests.gpu_util import DEV, rel_per_head
+from tests.gpu_util import DEV, Worst
 
 pytestmark = pytest.mark.gpu
 
@@ -38,15 +38,19 @@ def test_replay_harness_small(pool_dtype):
     o_ref, _, _, _ = ko.run_sequence(ex["q"], ex["k"], ex["v"], ex["g"], ex["b"], np.zeros((len(HEADS), 128, 128)))
     hsel = torch.as_tensor(HEADS, device=DEV)
     o_pre = wl.exact(t["o_pre"][:, hsel].cpu())
-    assert rel_per_head(o_pre, o_ref, 1) < 2e-2
+    w = Worst(2e-2)
+    w.out("prefill_o", o_pre, o_ref, 1)
 
     # the resumed outputs against the oracle run from the stored snapshot
     o_ver = wl.exact(t["o_ver"][:, :, hsel].cpu())                          # [n_ck, L, 2, d]
+    wv = Worst(2e-2)
     for i, c in enumerate(ckpts):
         s0 = np.swapaxes(wl.exact(t["pool"][slot_of[c]][hsel].cpu()), -1, -2)   # [2, d_k, d_v]
-        w = slice(c * C, c * C + L)
-        ov_ref, _, _, _ = ko.verify_ref(*(ex[n][w][None] for n in "qkvgb"), s0[None])
-        assert rel_per_head(o_ver[i], ov_ref[0], 1) < 2e-2
+        win = slice(c * C, c * C + L)
+        ov_ref, _, _, _ = ko.verify_ref(*(ex[n][win][None] for n in "qkvgb"), s0[None])
+        wv.out("verify_o", o_ver[i], ov_ref[0], 1)
+    w.check(f"replay harness pool={pool_dtype} prefill")
+    wv.check(f"replay harness pool={pool_dtype} resumed verify")
 
     # mutual difference and the harness's statistics
     diff = t["diff"]
