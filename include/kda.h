@@ -199,18 +199,39 @@ kda_status kda_commit(kda_pool pool, const int32_t* ckpt_slot, const int32_t* ds
  *             tokens that close block b0 -> slot of b0 (when m > 0), and the
  *             state after p + n tokens -> slot of b1.
  * Both are rebuilt, as in kda_commit, from the checkpoint in b0's slot and
- * the records of a verify call (one RNE cast each).  The running block of
- * the next step is b1.  block_size > L is required (KDA_ERR_INVALID_ARG
- * otherwise), so a window closes at most one block.  A request with n
- * outside [0, L] sets KDA_DEV_ERR_ACCEPT; one with p < 1, b1 beyond its
- * table row or a slot outside [0, n_slots) sets KDA_DEV_ERR_SLOT; either is
- * skipped.  The slots of different requests must be distinct.  block_table,
- * num_tokens, accepted_len: device arrays. */
+ * the records of a verify call (one RNE cast each).  block_size > L is
+ * required (KDA_ERR_INVALID_ARG otherwise), so a window closes at most one
+ * block.  A request with n outside [0, L] sets KDA_DEV_ERR_ACCEPT; one with
+ * p < 1, b1 beyond its table row or a slot outside [0, n_slots) sets
+ * KDA_DEV_ERR_SLOT; either is skipped.  The slots of different requests
+ * must be distinct.  block_table, num_tokens, accepted_len: device arrays.
+ *
+ * Post-processing for the next step ([P3] step 4: the align post-process
+ * moves the running block index on and resets the next step's copy bias to
+ * neutral), in the same launch, into the device arrays of `next` (each
+ * [n_req] int32, each optional: NULL fields are not written; none may alias
+ * an input):
+ *   num_tokens  p + n, the tokens the request holds after the commit (the
+ *               next call's num_tokens);
+ *   block       b1, the running block, whose slot holds the current state;
+ *   ckpt_slot   block_table[r][b1], the checkpoint the next verify reads;
+ *   copy_bias   0: the current state sits at the running block itself, so
+ *               the next step copies from no offset.
+ * A skipped request gets num_tokens = p, block = ckpt_slot = -1 (so a verify
+ * from that slot flags KDA_DEV_ERR_SLOT instead of reading a stale state)
+ * and copy_bias = 0. */
+typedef struct {
+  int32_t* num_tokens;
+  int32_t* block;
+  int32_t* ckpt_slot;
+  int32_t* copy_bias;
+} kda_align_next;
+
 kda_status kda_commit_align(kda_pool pool, const int32_t* block_table, int32_t blocks_per_req,
                             const int32_t* num_tokens, const int32_t* accepted_len,
                             int32_t block_size, const float* u_rec, const void* kg_rec,
                             int32_t rec_dtype, int32_t n_req, int32_t L, int32_t H, int32_t d_k,
-                            int32_t d_v, int32_t* dev_err, void* stream);
+                            int32_t d_v, kda_align_next next, int32_t* dev_err, void* stream);
 
 /* Rollback / fork ([P1] secs. 2-3; one launch for many slots as in the
  * fused slot copy of sec. 2): for every pair i, pool slot dst_slot[i]

@@ -40,6 +40,11 @@ class KdaPool(ctypes.Structure):
                 ("H", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32)]
 
 
+class KdaAlignNext(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_void_p), ("block", ctypes.c_void_p), ("ckpt_slot", ctypes.c_void_p),
+                ("copy_bias", ctypes.c_void_p)]
+
+
 class KdaConvTensor(ctypes.Structure):
     _fields_ = [("base", ctypes.c_void_p), ("slot_stride", ctypes.c_int64), ("n_slots", ctypes.c_int64),
                 ("rows", ctypes.c_int32), ("keep", ctypes.c_int32), ("dim", ctypes.c_int32),
@@ -60,7 +65,7 @@ _SIGS = {
                              _P, _P, _P, _U32, _P, _P],
     "kda_commit": [KdaPool, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P],
     "kda_commit_align": [KdaPool, _P, _I32, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
-                         _P, _P],
+                         KdaAlignNext, _P, _P],
     "kda_state_copy": [KdaPool, _P, _P, _I32, _P, _P],
     "kda_conv_state_update": [ctypes.POINTER(KdaConvTensor), _I32, _P, _P, _P, _I32, _P, _P],
     "kda_status_string": [_I32],
@@ -279,25 +284,38 @@ def commit(pool, ckpt_slot, accepted_len, u_rec, kg_rec, dst_slot=None, dev_err=
     _check(st, "kda_commit")
 
 
-def commit_align(pool, block_table, num_tokens, accepted_len, block_size, u_rec, kg_rec, dev_err=None):
-    """kda_commit_align: block-aligned commit; block_table is [n_req, blocks_per_req] int32."""
+def commit_align(pool, block_table, num_tokens, accepted_len, block_size, u_rec, kg_rec, dev_err=None,
+                 next_tokens=None, next_block=None, next_ckpt=None, copy_bias=None):
+    """kda_commit_align: block-aligned commit; block_table is [n_req, blocks_per_req] int32.
+    The optional int32 [n_req] outputs receive the next step's values (tokens
+    held, running block, its slot as the next checkpoint, a neutral copy
+    bias), written by the same launch."""
     n_req, H, L, dk, dv = _records(u_rec, kg_rec, pool)
     if block_table.dim() != 2 or block_table.shape[0] != n_req:
         raise ValueError(f"block_table must be [{n_req}, blocks_per_req], got {tuple(block_table.shape)}")
     _shape(num_tokens, "num_tokens", (n_req,))
     _shape(accepted_len, "accepted_len", (n_req,))
+    outs = (("next_tokens", next_tokens), ("next_block", next_block), ("next_ckpt", next_ckpt),
+            ("copy_bias", copy_bias))
+    for name, t in outs:
+        _shape(t, name, (n_req,))
     if dev_err is not None and dev_err.numel() < 1:
         raise ValueError("dev_err needs one element")
     _dev(block_table, "block_table", dtype=torch.int32, ndim=2)
-    for name, t in (("num_tokens", num_tokens), ("accepted_len", accepted_len), ("dev_err", dev_err)):
+    for name, t in (("num_tokens", num_tokens), ("accepted_len", accepted_len), ("dev_err", dev_err)) + outs:
         _dev(t, name, dtype=torch.int32)
     _dev(u_rec, "u_rec", dtype=torch.float32)
     _dev(kg_rec, "kg_rec")
     _same_device(pool, (("block_table", block_table), ("num_tokens", num_tokens),
-                        ("accepted_len", accepted_len), ("u_rec", u_rec), ("kg_rec", kg_rec), ("dev_err", dev_err)))
+                        ("accepted_len", accepted_len), ("u_rec", u_rec), ("kg_rec", kg_rec),
+                        ("dev_err", dev_err)) + outs)
+    for name, t in outs:   # the next-step arrays are written while the inputs are read
+        if t is not None and any(t.data_ptr() == x.data_ptr() for x in (num_tokens, accepted_len, block_table)):
+            raise ValueError(f"{name} must not alias an input")
+    nxt = KdaAlignNext(*(None if t is None else t.data_ptr() for _, t in outs))
     st = lib().kda_commit_align(_pool(pool), _ptr(block_table), block_table.shape[1], _ptr(num_tokens),
                                 _ptr(accepted_len), int(block_size), _ptr(u_rec), _ptr(kg_rec),
-                                DTYPE_CODES[kg_rec.dtype], n_req, L, H, dk, dv, _ptr(dev_err), _stream())
+                                DTYPE_CODES[kg_rec.dtype], n_req, L, H, dk, dv, nxt, _ptr(dev_err), _stream())
     _check(st, "kda_commit_align")
 
 

@@ -145,7 +145,7 @@ kda_status kda_commit_align(kda_pool pool, const int32_t* block_table, int32_t b
                             const int32_t* num_tokens, const int32_t* accepted_len,
                             int32_t block_size, const float* u_rec, const void* kg_rec,
                             int32_t rec_dtype, int32_t n_req, int32_t L, int32_t H, int32_t d_k,
-                            int32_t d_v, int32_t* dev_err, void* stream) {
+                            int32_t d_v, kda_align_next next, int32_t* dev_err, void* stream) {
   if (n_req < 0 || H <= 0 || L < 1 || blocks_per_req < 1) return KDA_ERR_INVALID_ARG;
   if (L > 256) return KDA_ERR_UNSUPPORTED;
   if (block_size <= L) return KDA_ERR_INVALID_ARG;   // a window would close more than one block
@@ -159,7 +159,8 @@ kda_status kda_commit_align(kda_pool pool, const int32_t* block_table, int32_t b
     return KDA_ERR_INVALID_ARG;
   if ((int64_t)n_req * H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
   kda::CommitAlignArgs a{pool_desc(pool), block_table, blocks_per_req, num_tokens, accepted_len, block_size,
-                         u_rec, kg_rec, rec_dtype, n_req, L, H, d_k, dev_err};
+                         u_rec, kg_rec, rec_dtype, n_req, L, H, d_k, next.num_tokens, next.block,
+                         next.ckpt_slot, next.copy_bias, dev_err};
   return launched(kda::launch_commit_align(a, static_cast<hipStream_t>(stream)));
 }
 

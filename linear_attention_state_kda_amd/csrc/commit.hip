@@ -138,27 +138,47 @@ __global__ __launch_bounds__(kT) void kda_commit_kernel(
 // b1 == b0 + 1: the state after the m = b1 bs - p accepted tokens that close
 // b0 into b0's slot (when m > 0), then S_{p+n} into b1's slot, continuing
 // from S_{p+m} in registers.
+// Post-processing for the next step (same summary, step 4: the running
+// block index moves on, the next step's copy bias goes back to neutral):
+// the head-0 workgroup of each request writes p + n, b1, b1's slot and a
+// zero bias to the optional next_* arrays (p, -1, -1, 0 for a request that
+// is skipped).
+struct AlignNext {
+  int32_t *tokens, *block, *ckpt, *bias;
+};
+
 template <typename TPool, typename TRec>
 __global__ __launch_bounds__(kT) void kda_commit_align_kernel(
     TPool* __restrict__ pool, int64_t n_slots, const int32_t* __restrict__ table, int blocks_per_req,
     const int32_t* __restrict__ num_tokens, const int32_t* __restrict__ accepted, int bs,
     const float* __restrict__ u_rec, const TRec* __restrict__ kg_rec, int n_req, int L, int H,
-    int32_t* __restrict__ dev_err) {
+    AlignNext nx, int32_t* __restrict__ dev_err) {
   __shared__ CommitSmem sm;
   const int r = blockIdx.x / H, h = blockIdx.x % H;
   if (r >= n_req) return;
   const int n = accepted[r], p = num_tokens[r];
+  const bool post = threadIdx.x == 0 && h == 0;
+  auto publish = [&](int tokens, int block, int slot) {
+    if (!post) return;
+    if (nx.tokens) nx.tokens[r] = tokens;
+    if (nx.block) nx.block[r] = block;
+    if (nx.ckpt) nx.ckpt[r] = slot;
+    if (nx.bias) nx.bias[r] = 0;
+  };
   if (n < 0 || n > L) {
-    if (threadIdx.x == 0 && h == 0) set_err(dev_err, 1u << 2);
+    if (post) set_err(dev_err, 1u << 2);
+    publish(p, -1, -1);
     return;
   }
   const int b0 = p >= 1 ? (p - 1) / bs : 0, b1 = p >= 1 ? (p + n - 1) / bs : 0;
   const int s0 = p >= 1 && b1 < blocks_per_req ? table[(int64_t)r * blocks_per_req + b0] : -1;
   const int s1 = p >= 1 && b1 < blocks_per_req ? table[(int64_t)r * blocks_per_req + b1] : -1;
   if (s0 < 0 || (int64_t)s0 >= n_slots || s1 < 0 || (int64_t)s1 >= n_slots) {
-    if (threadIdx.x == 0 && h == 0) set_err(dev_err, 1u);
+    if (post) set_err(dev_err, 1u);
+    publish(p, -1, -1);
     return;
   }
+  publish(p + n, b1, s1);
   if (n == 0) return;
   const int64_t rec0 = ((int64_t)r * H + h) * L;
   const int m = b1 != b0 ? b1 * bs - p : 0;   // accepted tokens that close block b0
@@ -199,7 +219,8 @@ hipError_t align_by_rec(const CommitAlignArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((kda_commit_align_kernel<TPool, TR>), grid, block, 0, st,                      \
                      static_cast<TPool*>(a.pool.base), a.pool.n_slots, a.block_table, a.blocks_per_req, \
                      a.num_tokens, a.accepted_len, a.block_size, a.u_rec,                           \
-                     static_cast<const TR*>(a.kg_rec), a.n_req, a.L, a.H, a.dev_err)
+                     static_cast<const TR*>(a.kg_rec), a.n_req, a.L, a.H,                           \
+                     AlignNext{a.next_tokens, a.next_block, a.next_ckpt, a.next_bias}, a.dev_err)
   switch (a.rec_dtype) {
     case F32: KDA_COMMIT_ALIGN_LAUNCH(float); break;
     case F16: KDA_COMMIT_ALIGN_LAUNCH(f16); break;

@@ -75,6 +75,7 @@ struct CommitAlignArgs {
   const void* kg_rec;
   int rec_dtype;
   int n_req, L, H, d;
+  int32_t *next_tokens, *next_block, *next_ckpt, *next_bias;   // optional outputs [n_req]
   int32_t* dev_err;
 };
 

@@ -72,9 +72,12 @@ int main(void) {
   expect("commit null accepted", kda_commit(pool, fi, NULL, NULL, (const float*)fake, fake, KDA_BF16, 4, 8, 2, 128, 128, NULL, NULL), KDA_ERR_INVALID_ARG);
   expect("commit L 300", kda_commit(pool, fi, NULL, fi, (const float*)fake, fake, KDA_BF16, 4, 300, 2, 128, 128, NULL, NULL), KDA_ERR_UNSUPPORTED);
   expect("commit nothing to do", kda_commit(pool, fi, NULL, fi, (const float*)fake, fake, KDA_BF16, 0, 8, 2, 128, 128, NULL, NULL), KDA_OK);
-  expect("align block <= L", kda_commit_align(pool, fi, 4, fi, fi, 8, (const float*)fake, fake, KDA_BF16, 4, 8, 2, 128, 128, NULL, NULL), KDA_ERR_INVALID_ARG);
-  expect("align null table", kda_commit_align(pool, NULL, 4, fi, fi, 64, (const float*)fake, fake, KDA_BF16, 4, 8, 2, 128, 128, NULL, NULL), KDA_ERR_INVALID_ARG);
-  expect("align nothing to do", kda_commit_align(pool, fi, 4, fi, fi, 64, (const float*)fake, fake, KDA_BF16, 0, 8, 2, 128, 128, NULL, NULL), KDA_OK);
+  {
+    kda_align_next nx = {(int32_t*)fake, NULL, (int32_t*)fake, NULL};
+    expect("align block <= L", kda_commit_align(pool, fi, 4, fi, fi, 8, (const float*)fake, fake, KDA_BF16, 4, 8, 2, 128, 128, nx, NULL, NULL), KDA_ERR_INVALID_ARG);
+    expect("align null table", kda_commit_align(pool, NULL, 4, fi, fi, 64, (const float*)fake, fake, KDA_BF16, 4, 8, 2, 128, 128, nx, NULL, NULL), KDA_ERR_INVALID_ARG);
+    expect("align nothing to do", kda_commit_align(pool, fi, 4, fi, fi, 64, (const float*)fake, fake, KDA_BF16, 0, 8, 2, 128, 128, nx, NULL, NULL), KDA_OK);
+  }
 
   /* copy */
   expect("copy n < 0", kda_state_copy(pool, fi, fi, -1, NULL, NULL), KDA_ERR_INVALID_ARG);

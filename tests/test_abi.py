@@ -138,8 +138,8 @@ def test_commit_align_host_errors(L):
     P = pool()
     ca = lambda **kw: L.kda_commit_align(*[kw.get(n, d) for n, d in [
         ("pool", P), ("bt", FAKE), ("bpr", 4), ("nt", FAKE), ("acc", FAKE), ("bs", 64), ("u", FAKE),
-        ("kg", FAKE), ("rdt", 2), ("n", 4), ("L", 8), ("H", 2), ("dk", 128), ("dv", 128), ("err", None),
-        ("st", None)]])
+        ("kg", FAKE), ("rdt", 2), ("n", 4), ("L", 8), ("H", 2), ("dk", 128), ("dv", 128),
+        ("nx", kda.KdaAlignNext(None, None, None, None)), ("err", None), ("st", None)]])
     assert ca(bs=8) == 1            # a window of 8 could close two blocks of 8
     assert ca(bs=9, n=0) == 0
     assert ca(bpr=0) == 1

@@ -38,8 +38,14 @@ def run_case(pool_dtype, block_size, p, n, H=4, L=8, blocks=4, seed=61):
     torch.cuda.synchronize()
     assert err.item() == 0
     before = pool.clone()
-    kda.commit_align(pool, i32(table), i32(p), i32(n), block_size, u_rec, kg_rec, dev_err=err)
+    nxt = [torch.full((n_req,), 12345, dtype=torch.int32, device=DEV) for _ in range(4)]
+    kda.commit_align(pool, i32(table), i32(p), i32(n), block_size, u_rec, kg_rec, dev_err=err,
+                     next_tokens=nxt[0], next_block=nxt[1], next_ckpt=nxt[2], copy_bias=nxt[3])
     torch.cuda.synchronize()
+    # the next step's values: bitwise what the oracle's post-processing gives
+    want_next = ko.align_next_ref(table, p, n, block_size, L, pool.shape[0])
+    for got, want in zip(nxt, want_next):
+        assert np.array_equal(got.cpu().numpy(), want), (got, want)
     for r in range(n_req):
         for b in range(blocks):
             slots.setdefault(int(table[r][b]), np.full((H, d, d), np.nan))
@@ -48,7 +54,7 @@ def run_case(pool_dtype, block_size, p, n, H=4, L=8, blocks=4, seed=61):
     writes, want_err = ko.commit_align_ref(slots, table, p, n, block_size, kg64[..., :d], kg64[..., d:],
                                            u_rec.cpu().double().numpy())
     return dict(pool=pool, before=before, writes=writes, err=err.item(), want_err=want_err, toks=toks, S0=S0,
-                table=table, ck=ck)
+                table=table, ck=ck, next=[t.cpu().numpy() for t in nxt])
 
 
 @pytest.mark.parametrize("pool_dtype", ["f32", "bf16", "f16"])
@@ -96,6 +102,7 @@ def test_commit_align_errors():
     p, n = [5, 0, 33, 10], [9, 1, 8, 3]
     r = run_case("f32", bs, p, n, seed=63)
     assert r["err"] == kda.DEV_ERR_ACCEPT | kda.DEV_ERR_SLOT == r["want_err"]
+    assert list(r["next"][1]) == [-1, -1, -1, 1] and list(r["next"][2][:3]) == [-1, -1, -1]
     written = set(r["writes"])
     assert written == {int(r["table"][3][1])}
     for slot in range(r["pool"].shape[0]):
@@ -119,3 +126,60 @@ def test_commit_align_short_window():
         else:
             assert torch.equal(r["pool"][slot], r["before"][slot]), slot
     w.check("commit_align L=3 block 4")
+
+
+@pytest.mark.parametrize("pool_dtype", ["f32", "bf16"])
+def test_commit_align_chain_from_running_block(pool_dtype):
+    """Three speculative steps on the device alone: each verify reads the
+    checkpoint slot the previous align commit wrote to ``next_ckpt``, and
+    each align commit takes ``next_tokens`` as its token count, with no
+    host arithmetic in between; every written state then equals a replay of
+    the accepted tokens of all steps so far, and the slots of finished
+    blocks hold the state at their last token."""
+    H, d, L, bs, n_req, blocks = 4, 128, 8, 12, 5, 5
+    seed = 71
+    p0 = np.array([1, 5, 11, 12, 20], dtype=np.int32)
+    table = (np.arange(n_req * blocks, dtype=np.int32).reshape(n_req, blocks) * 3 + 2).astype(np.int32)
+    pool = make_pool(int(table.max()) + 1, H, d, d, pool_dtype)
+    S0 = []
+    for r in range(n_req):
+        s0 = int(table[r][(p0[r] - 1) // bs])
+        st = wl.pool_state(s0, H, d, d, pool_dtype, seed)
+        pool[s0] = st.to(DEV)
+        S0.append(np.swapaxes(wl.exact(st), -1, -2))
+    accepted = np.random.default_rng([seed, 1]).integers(0, L + 1, (3, n_req)).astype(np.int32)
+    accepted[0, 2] = L                              # request 2 closes its first block in step 0
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    tok = i32(p0)
+    ck = i32([int(table[r][(p0[r] - 1) // bs]) for r in range(n_req)])
+    tbl = i32(table)
+    steps = []
+    for step in range(3):
+        toks = wl.token_inputs(n_req * L, H, d, d, "bf16", seed + 10 + step, shape_prefix=(n_req, L))
+        steps.append(toks)
+        dev = {x: toks[x].to(DEV) for x in "qkvgb"}
+        _, u_rec, kg_rec = kda.recurrent_verify(dev["q"], dev["k"], dev["v"], dev["g"], dev["b"], pool, ck,
+                                                dev_err=err)
+        nt, nb, nc, bias = (torch.empty(n_req, dtype=torch.int32, device=DEV) for _ in range(4))
+        kda.commit_align(pool, tbl, tok, i32(accepted[step]), bs, u_rec, kg_rec, dev_err=err,
+                         next_tokens=nt, next_block=nb, next_ckpt=nc, copy_bias=bias)
+        tok, ck = nt, nc
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert np.array_equal(tok.cpu().numpy(), p0 + accepted.sum(axis=0))
+    assert not bias.cpu().numpy().any()
+    w = Worst(1e-4 if pool_dtype == "f32" else 2e-2)
+    for r in range(n_req):
+        ex = {x: np.concatenate([wl.exact(steps[s][x][r])[:accepted[s, r]] for s in range(3)]) for x in "qkvgb"}
+        total = int(accepted[:, r].sum())
+        p_end = int(p0[r]) + total
+        # the running block's slot: the state after all accepted tokens
+        rep = ko.replay_ref(*(ex[x] for x in "qkvgb"), S0[r], total)
+        assert int(ck[r].item()) == int(table[r][(p_end - 1) // bs])
+        w.state("current", to_math(pool[int(ck[r].item())]), rep)
+        # every block finished along the way: the state at its last token
+        for b in range((int(p0[r]) - 1) // bs, (p_end - 1) // bs):
+            last = (b + 1) * bs
+            rep_b = ko.replay_ref(*(ex[x] for x in "qkvgb"), S0[r], last - int(p0[r]))
+            w.state("block_end", to_math(pool[int(table[r][b])]), rep_b)
+    w.check(f"commit_align three-step chain pool={pool_dtype}")

@@ -7,9 +7,10 @@
 * Split invariance: prefilling T1 = 4 full chunks, then the rest of the
   sequence from the final state left in an fp32 pool slot, reproduces the
   one-shot run bit for bit (the same chunks meet the same fp32 state).
-* Graph capture: prefill, verify, commit and copy captured once in a HIP
-  graph and replayed three times, with eager work and synchronisations in
-  between, reproduce the eager results bit for bit each time.
+* Graph capture: prefill, verify, commit, align commit (with its next-step
+  outputs), copy and the conv-state update captured once in a HIP graph and
+  replayed three times, with eager work and synchronisations in between,
+  reproduce the eager results bit for bit each time.
 """
 
 import numpy as np
@@ -97,6 +98,19 @@ def test_graph_capture_replay():
     kg_rec = torch.empty((n_req, H, L, 2 * D), dtype=torch.bfloat16, device=DEV)
     args = dict(init=i32([0, -1]), final=i32([4, 5]), ptr=i32([0, 1, 1]), tc=i32([2]), ts=i32([6]),
                 ckpt=i32([0, 1, 2, 3]), acc=i32([8, 0, 3, 5]), src=i32([0, 2]), dst=i32([7, 8]))
+    # align commit on a pool of its own: tables of 2 blocks of 12 tokens per request
+    apool0 = make_pool(12, H, D, D, "f32")
+    for s in range(4):
+        apool0[s] = wl.pool_state(20 + s, H, D, D, "f32", 43).to(DEV)
+    apool = apool0.clone()
+    a_table = i32([[0, 4], [1, 5], [2, 6], [3, 7]])
+    a_tok, a_acc = i32([5, 10, 12, 1]), i32([8, 3, 4, 0])
+    a_next = [torch.zeros(n_req, dtype=torch.int32, device=DEV) for _ in range(4)]
+    # conv windows: two tensors, a fork copy, an in-place compaction and a clear
+    conv0 = [(torch.arange(8 * 11 * 256, device=DEV, dtype=torch.float32).reshape(8, 11, 256) % 977).to(torch.bfloat16),
+             torch.arange(8 * 6 * 64, device=DEV, dtype=torch.float32).reshape(8, 6, 64) * 0.5]
+    conv = [t.clone() for t in conv0]
+    c_dst, c_src, c_shift = i32([1, 2, 3]), i32([0, 2, -1]), i32([0, 2, 0])
 
     def calls():
         kda.chunk_prefill(ptoks["q"], ptoks["k"], ptoks["v"], ptoks["g"], ptoks["b"], cu, C, pool,
@@ -105,9 +119,12 @@ def test_graph_capture_replay():
         kda.recurrent_verify(stoks["q"], stoks["k"], stoks["v"], stoks["g"], stoks["b"], pool,
                              args["ckpt"], o=o_v, u_rec=u_rec, kg_rec=kg_rec)
         kda.commit(pool, args["ckpt"], args["acc"], u_rec, kg_rec)
+        kda.commit_align(apool, a_table, a_tok, a_acc, 12, u_rec, kg_rec, next_tokens=a_next[0],
+                         next_block=a_next[1], next_ckpt=a_next[2], copy_bias=a_next[3])
         kda.state_copy(pool, args["src"], args["dst"])
+        kda.conv_state_update(conv, [3, 2], c_dst, c_src, c_shift)
 
-    outs = (o_p, track_f32, o_v, u_rec, kg_rec, pool)
+    outs = (o_p, track_f32, o_v, u_rec, kg_rec, *a_next, pool, apool, *conv)
     calls()
     torch.cuda.synchronize()
     eager = [t.clone() for t in outs]
@@ -116,6 +133,9 @@ def test_graph_capture_replay():
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         pool.copy_(pool0)
+        apool.copy_(apool0)
+        for t, t0 in zip(conv, conv0):
+            t.copy_(t0)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
@@ -124,7 +144,10 @@ def test_graph_capture_replay():
     torch.cuda.synchronize()
     for rep in range(3):
         pool.copy_(pool0)                 # eager work between replays
-        for t in outs[:-1]:
+        apool.copy_(apool0)
+        for t, t0 in zip(conv, conv0):
+            t.copy_(t0)
+        for t in outs[:9]:
             t.zero_()
         torch.cuda.synchronize()
         graph.replay()
