@@ -98,6 +98,19 @@ typedef enum { KDA_F32 = 0, KDA_F16 = 1, KDA_BF16 = 2 } kda_dtype;
 #define KDA_DEV_ERR_ACCEPT 4u /* an accepted length outside [0, L] */
 #define KDA_DEV_ERR_SEQLEN 8u /* cu_seqlens decreasing, negative, or beyond total_tokens */
 #define KDA_DEV_ERR_SHIFT 16u /* a conv-state shift outside [0, rows - keep] */
+#define KDA_DEV_ERR_GATE 32u  /* a gate beyond the supported range (below): results not exact */
+
+/* Supported gate range.  The chunked prefill scales keys by e^-Gamma, Gamma
+ * being the cumulative log decay (sum of g) since the start of the chunk,
+ * and rounds the result to the operand type: with |k| <= 1 elementwise that
+ * stays finite while every chunk's cumulative log decay stays above about
+ * -11 with fp16 inputs (65504 = e^11.09), about -88 with bf16 inputs, and
+ * about -87 with fp32 inputs (chunk 16).  verify forms the same factor over
+ * each block of 8 positions in fp32, finite while a block's summed gate stays
+ * above about -88.  A chunk or block beyond that sets KDA_DEV_ERR_GATE in
+ * *dev_err (its results are then not to be used); inside it the results meet
+ * the usual bars.  The workloads' gates, g in [-0.1, -0.001], give at most
+ * -6.4 per chunk. */
 
 /* A slot-indexed state pool, passed by value.  base points to
  * n_slots * H * d_v * d_k elements of `dtype` (a kda_dtype value). */

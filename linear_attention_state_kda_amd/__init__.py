@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "KdaError", "lib", "DTYPE_CODES", "DEV_ERR_SLOT", "DEV_ERR_TRACK", "DEV_ERR_ACCEPT",
-    "DEV_ERR_SEQLEN", "DEV_ERR_SHIFT", "QK_L2NORM", "prefill_workspace_bytes", "chunk_prefill", "recurrent_verify",
+    "DEV_ERR_SEQLEN", "DEV_ERR_SHIFT", "DEV_ERR_GATE", "QK_L2NORM", "prefill_workspace_bytes", "chunk_prefill", "recurrent_verify",
     "commit", "commit_align", "state_copy", "conv_state_update", "LIB_PATH",
 ]
 
@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED",
           3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_LAUNCH"}
-DEV_ERR_SLOT, DEV_ERR_TRACK, DEV_ERR_ACCEPT, DEV_ERR_SEQLEN, DEV_ERR_SHIFT = 1, 2, 4, 8, 16
+DEV_ERR_SLOT, DEV_ERR_TRACK, DEV_ERR_ACCEPT, DEV_ERR_SEQLEN, DEV_ERR_SHIFT, DEV_ERR_GATE = 1, 2, 4, 8, 16, 32
 QK_L2NORM = 1   # flags bit of kda_chunk_prefill / kda_recurrent_verify
 
 

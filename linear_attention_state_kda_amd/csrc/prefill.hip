@@ -116,7 +116,8 @@ template <int DK, int C, typename TIn, typename TOp>
 __global__ __launch_bounds__(kThreads) void kda_chunk_prep(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ g,
     const TIn* __restrict__ bl, const int32_t* __restrict__ cu, int n_seqs, int64_t total,
-    int H, int64_t cap, const int32_t* __restrict__ off, uint8_t* __restrict__ recs, int l2norm) {
+    int H, int64_t cap, const int32_t* __restrict__ off, uint8_t* __restrict__ recs, int l2norm,
+    int32_t* __restrict__ dev_err) {
   typedef PrepSmem<DK, C, TOp> Sm;
   typedef Rec<DK, C, TOp> R;
   constexpr int KBK = R::KBK, KBT = R::KBT;
@@ -232,14 +233,21 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_prep(
 #pragma unroll
     for (int e = 0; e < 4; ++e) inv_total[e] = 1.0f / total_dec[e];
     const int kp = pos_of<KBK>(4 * cq);
+    // e^-Gamma_t grows with the chunk's decay: an element of K e^-Gamma that
+    // is not finite in fp32 (cumulative log decay below about -87 within a
+    // chunk) sets the gate-range error bit
+    bool range_ok = true;
 #pragma unroll
     for (int jj = 0; jj < Sm::TPG; ++jj) {
       const int t = tg * Sm::TPG + jj;
       const floatx4 epos = pre * fw[jj];                 // e^Gamma_t
       const floatx4 erem = bw[jj] * post;                // e^(Gamma_n - Gamma_t)
       const floatx4 eneg = erem * inv_total;             // e^-Gamma_t
+      const floatx4 khv = kv[jj] * eneg;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) range_ok = range_ok && __builtin_fabsf(khv[e]) <= 3.40282347e38f;
       store4(&sm.u.a.kt[t * Sm::LDK + kp], kv[jj] * epos);
-      store4(&sm.u.a.kh[t * Sm::LDK + kp], kv[jj] * eneg);
+      store4(&sm.u.a.kh[t * Sm::LDK + kp], khv);
       store4(&sm.u.a.qt[t * Sm::LDK + kp], qv[jj] * epos);
       const floatx4 kb = kv[jj] * erem;
       const int tp = pos_of<KBT>(t);
@@ -247,6 +255,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_prep(
       for (int e = 0; e < 4; ++e) sm.u.a.kbt[(4 * cq + e) * Sm::LDT + tp] = from_f32<TOp>(kb[e]);
     }
     if (tg == 0) *reinterpret_cast<floatx4*>(rec + R::kDec + 16 * cq) = total_dec;
+    if (!range_ok) set_err(dev_err, 1u << 5);
   }
   __syncthreads();
 
@@ -739,7 +748,8 @@ hipError_t run(const PrefillArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(kp, dim3((unsigned)(w.cap * a.H)), dim3(kThreads), smp, st,
                        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                        static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.b), a.cu_seqlens,
-                       a.n_seqs, a.total_tokens, a.H, w.cap, w.off, w.recs, (a.flags & 1u) ? 1 : 0);
+                       a.n_seqs, a.total_tokens, a.H, w.cap, w.off, w.recs, (a.flags & 1u) ? 1 : 0,
+                       a.dev_err);
   }
   auto ks = kda_chunk_scan<DK, DV, C, TIn, TOp, TPool>;
   const int64_t pairs = (int64_t)a.n_seqs * a.H;

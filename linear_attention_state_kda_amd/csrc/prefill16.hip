@@ -143,7 +143,8 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void kda_chunk_prep16(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ g,
     const T* __restrict__ bl, const int32_t* __restrict__ cu, int n_seqs, int64_t total,
-    int H, int64_t cap, const int32_t* __restrict__ off, uint8_t* __restrict__ recs, int l2norm) {
+    int H, int64_t cap, const int32_t* __restrict__ off, uint8_t* __restrict__ recs, int l2norm,
+    int32_t* __restrict__ dev_err) {
   constexpr int DK = 128, C = 64, NFK = DK / 32;
   typedef Rec16 R;
   typedef typename OpTraits<T>::frag F8;   // 8 x 16-bit fragment
@@ -283,8 +284,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   }
   __syncthreads();
 
-  // ---- Kt = K e^Gamma, Qt = Q e^Gamma, Kb = K e^(Gamma_n - Gamma), Kh = Kb e^-Gamma_n
+  // ---- Kt = K e^Gamma, Qt = Q e^Gamma, Kb = K e^(Gamma_n - Gamma), Kh = Kb e^-Gamma_n.
+  //      Every factor but Kh's is at most 1.  Kh = K e^-Gamma grows with the
+  //      chunk's decay; an element that would round to infinity in T (a
+  //      chunk whose cumulative log decay falls below about -11 for fp16, or
+  //      leaves the fp32 range, below about -88, for bf16, at |k| <= 1) is
+  //      flagged with the gate-range error bit instead of passing silently.
   F8 ktf[NFK], qtf[NFK], kbf[NFK], khf[NFK];
+  // smallest fp32 magnitude that rounds to infinity in T (RNE): halfway
+  // between T's largest finite value and the next power of two
+  constexpr float kInf16 = std::is_same<T, f16>::value ? 65520.f : __builtin_bit_cast(float, 0x7F7F8000u);
+  bool range_ok = true;
 #pragma unroll
   for (int kb = 0; kb < NFK; ++kb)
 #pragma unroll
@@ -300,12 +310,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
         const float kv = to_f32(kr[kb][hf][e]);
         const float qv = to_f32(qr[kb][hf][e]);
         const float kbv = kv * b;
+        const float khv = kbv * ni[e];
+        range_ok = range_ok && __builtin_fabsf(khv) < kInf16;   // false for inf and NaN too
         ktf[kb][4 * hf + e] = from_f32<T>(kv * a);
         qtf[kb][4 * hf + e] = from_f32<T>(qv * a);
         kbf[kb][4 * hf + e] = from_f32<T>(kbv);
-        khf[kb][4 * hf + e] = from_f32<T>(kbv * ni[e]);
+        khf[kb][4 * hf + e] = from_f32<T>(khv);
       }
     }
+  if (__builtin_amdgcn_ballot_w64(!range_ok) != 0 && lane == 0) set_err(dev_err, 1u << 5);
   // Records are stored non-temporally, in whole 16-byte fragment pieces
   // (Z and Pw are assembled in LDS first): the scan reads each record once,
   // about a prep's duration later, and dirty records left in the
@@ -839,7 +852,7 @@ hipError_t run16(const PrefillArgs& a, hipStream_t st, int64_t cap, const int32_
     hipLaunchKernelGGL(kda_chunk_prep16<TIn>, dim3((unsigned)(cap * a.H)), dim3(kThreads), 0, st,
                        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                        static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.b), a.cu_seqlens,
-                       a.n_seqs, a.total_tokens, a.H, cap, off, recs, (a.flags & 1u) ? 1 : 0);
+                       a.n_seqs, a.total_tokens, a.H, cap, off, recs, (a.flags & 1u) ? 1 : 0, a.dev_err);
   const int64_t pairs = (int64_t)a.n_seqs * a.H;
   const int64_t pairs8 = (pairs + kXcd - 1) / kXcd * kXcd;
   // Each workgroup streams its head's whole record per chunk through its

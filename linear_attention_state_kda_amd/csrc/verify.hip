@@ -225,6 +225,9 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(resident_wgs
         s_ku[jj][c] = kk * Di;
       }
       if (hh) s_dec[c] = D;  // read only when the block is full (a next block exists)
+      // 1/D grows with the block's decay: past the fp32 range (a summed gate
+      // below about -88 over the block's positions) the gate-range bit is set
+      if (!(Di <= 3.40282347e38f)) set_err(dev_err, 1u << 5);
     }
     __syncthreads();
     // ---- Gram partial of wave w over keys 32 w .. 32 w + 31: rows s (8 of

@@ -63,7 +63,7 @@ def rel_per_head(x, ref, head_axis):
     return max(rel(a, b) for a, b in zip(xs, rs))
 
 
-def row_errors(x, ref, head_axis):
+def row_errors(x, ref, head_axis, floor=None):
     """Row metric of ``x`` against ``ref``; rows run along the last axis and
     ``head_axis`` (not the last) names the head axis.  Returns a dict:
     ``row`` the worst floored row error, ``row_raw`` the worst unfloored
@@ -78,7 +78,7 @@ def row_errors(x, ref, head_axis):
     err = np.linalg.norm(xs - rs, axis=-1)            # (heads, rows)
     nrm = np.linalg.norm(rs, axis=-1)
     rms = np.sqrt(np.mean(nrm * nrm, axis=-1, keepdims=True))
-    den = np.maximum(nrm, ROW_FLOOR * rms)
+    den = np.maximum(nrm, (ROW_FLOOR if floor is None else floor) * rms)
     with np.errstate(divide="ignore", invalid="ignore"):
         floored = np.where(den > 0, err / den, np.where(err > 0, np.inf, 0.0))
         raw = np.where(nrm > 0, err / nrm, np.where(err > 0, np.inf, 0.0))
@@ -91,17 +91,18 @@ def row_errors(x, ref, head_axis):
                 raw_at_norm=float(nrm[hw, rw]) / r, raw_at_err=float(err[hw, rw]) / r)
 
 
-def state_rows(S, S_ref):
+def state_rows(S, S_ref, floor=None):
     """Row metric of states in the oracle's (H, d_k, d_v) orientation, one
     row per pool row (value column of S)."""
-    return row_errors(np.swapaxes(S, -1, -2), np.swapaxes(S_ref, -1, -2), 0)
+    return row_errors(np.swapaxes(S, -1, -2), np.swapaxes(S_ref, -1, -2), 0, floor)
 
 
 class Worst:
     """Running maxima of the metrics of a test, asserted against one bar."""
 
-    def __init__(self, tol):
+    def __init__(self, tol, floor=None):
         self.tol = tol
+        self.floor = floor   # row floor in units of the head's rms row norm (ROW_FLOOR if None)
         self.m = {}
 
     def add(self, key, stats):
@@ -121,17 +122,18 @@ class Worst:
     def out(self, key, x, ref, head_axis):
         """Per-head Frobenius and row metrics of an output block."""
         self.add(key, rel_per_head(x, ref, head_axis))
-        self.add(key, row_errors(x, ref, head_axis))
+        self.add(key, row_errors(x, ref, head_axis, self.floor))
 
     def state(self, key, S, S_ref):
         """Per-head Frobenius and row metrics of (H, d_k, d_v) states."""
         self.add(key, rel_per_head(S, S_ref, 0))
-        self.add(key, state_rows(S, S_ref))
+        self.add(key, state_rows(S, S_ref, self.floor))
 
     def check(self, label=""):
         """Assert every Frobenius and floored row metric is under the bar
         (the unfloored row and absmax numbers are reported only)."""
-        print(f"[parity] {label} tol={self.tol:g} " +
+        fl = ROW_FLOOR if self.floor is None else self.floor
+        print(f"[parity] {label} tol={self.tol:g} floor={fl:g} " +
               " ".join(f"{k}={v:.3g}" for k, v in sorted(self.m.items())), flush=True)
         for k, v in self.m.items():
             if k.split(".")[-1] in ("row_raw", "absmax", "raw_at_norm", "raw_at_err"):
