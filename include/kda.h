@@ -29,7 +29,8 @@
  * Conventions shared by every call
  *  - Every pointer except `stream` and the pool struct itself is a DEVICE
  *    pointer.  The caller owns all buffers; the library keeps no pointer
- *    after a call returns and holds no global mutable state.
+ *    after a call returns and holds no global mutable state (the one
+ *    exception is kda_chunk_prefill_noalloc's static scratch, below).
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *    stream).  No call reads device memory back to the host, none allocates,
  *    and none synchronises, so all of them can be captured in a HIP graph.
@@ -163,6 +164,31 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
                              const int32_t* track_slot, int32_t n_track, float* track_f32,
                              uint32_t flags, int32_t* dev_err, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* Allocation-free variant of kda_chunk_prefill, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, layouts, checks
+ * and results as kda_chunk_prefill, without the workspace: the chunk map and
+ * records live in a static device array of the library,
+ * KDA_NOALLOC_SCRATCH_BYTES (256 MiB) per GPU, held by every GPU the
+ * library runs on until the process ends (the single-layer workload,
+ * 8229 tokens x 32 heads, takes 230 MB of it).  A call whose workspace
+ * (kda_chunk_prefill_workspace) exceeds that returns KDA_ERR_WORKSPACE
+ * before any launch.  The call allocates nothing; its first call on a
+ * device resolves the array's address there (no allocation), so a caller
+ * that captures graphs makes one call before capturing.  Every call on a
+ * GPU shares that GPU's array and leaves its last contents there (nothing in
+ * it needs to start at zero): calls that overlap on one GPU, from different
+ * streams or threads, race on it and must be serialised by the caller. */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+kda_status kda_chunk_prefill_noalloc(const void* q, const void* k, const void* v, const void* g,
+                                     const void* b, int32_t in_dtype, void* o,
+                                     const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens,
+                                     int32_t H, int32_t d_k, int32_t d_v, int32_t chunk, kda_pool pool,
+                                     const int32_t* init_slot, const int32_t* final_slot,
+                                     const int32_t* track_ptr, const int32_t* track_chunk,
+                                     const int32_t* track_slot, int32_t n_track, float* track_f32,
+                                     uint32_t flags, int32_t* dev_err, void* stream);
 
 /* Speculative-decode verify ([P3] step 3): per request, read the checkpoint
  * in pool slot ckpt_slot[r] (never written), run the token recurrence over

@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "KdaError", "lib", "DTYPE_CODES", "DEV_ERR_SLOT", "DEV_ERR_TRACK", "DEV_ERR_ACCEPT",
     "DEV_ERR_SEQLEN", "DEV_ERR_SHIFT", "DEV_ERR_GATE", "QK_L2NORM", "prefill_workspace_bytes", "chunk_prefill", "recurrent_verify",
-    "commit", "commit_align", "state_copy", "conv_state_update", "LIB_PATH",
+    "commit", "commit_align", "state_copy", "conv_state_update", "chunk_prefill_noalloc",
+    "NOALLOC_SCRATCH_BYTES", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -27,6 +28,7 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED",
           3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_LAUNCH"}
 DEV_ERR_SLOT, DEV_ERR_TRACK, DEV_ERR_ACCEPT, DEV_ERR_SEQLEN, DEV_ERR_SHIFT, DEV_ERR_GATE = 1, 2, 4, 8, 16, 32
 QK_L2NORM = 1   # flags bit of kda_chunk_prefill / kda_recurrent_verify
+NOALLOC_SCRATCH_BYTES = 256 << 20   # KDA_NOALLOC_SCRATCH_BYTES
 
 
 class KdaError(RuntimeError):
@@ -61,6 +63,8 @@ _SIGS = {
     "kda_chunk_prefill_workspace": [_I32, _I64, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)],
     "kda_chunk_prefill": [_P, _P, _P, _P, _P, _I32, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32,
                           KdaPool, _P, _P, _P, _P, _P, _I32, _P, _U32, _P, _P, _SZ, _P],
+    "kda_chunk_prefill_noalloc": [_P, _P, _P, _P, _P, _I32, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32,
+                                  KdaPool, _P, _P, _P, _P, _P, _I32, _P, _U32, _P, _P],
     "kda_recurrent_verify": [_P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, KdaPool,
                              _P, _P, _P, _U32, _P, _P],
     "kda_commit": [KdaPool, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P],
@@ -147,12 +151,10 @@ def prefill_workspace_bytes(n_seqs, total_tokens, H, d_k, d_v, chunk, in_dtype):
     return int(out.value)
 
 
-def chunk_prefill(q, k, v, g, b, cu_seqlens, chunk, pool, init_slot, final_slot,
-                  track_ptr=None, track_chunk=None, track_slot=None, track_f32=None,
-                  o=None, dev_err=None, workspace=None, qk_l2norm=False):
-    """kda_chunk_prefill on packed token tensors q, k, g [T, H, d_k], v [T, H, d_v],
-    b [T, H]; returns o [T, H, d_v] (allocated when not given).  qk_l2norm sets
-    KDA_QK_L2NORM (q and k normalised inside the kernel)."""
+def _prefill_marshal(q, k, v, g, b, cu_seqlens, chunk, pool, init_slot, final_slot, track_ptr, track_chunk,
+                     track_slot, track_f32, o, dev_err, workspace, qk_l2norm):
+    """Checks of a prefill call; returns (o, the C arguments before the
+    workspace).  ``workspace`` False means the call takes none."""
     if q.dim() != 3 or v.dim() != 3:
         raise ValueError("q and v must be [T, H, d]")
     T, H, dk = q.shape
@@ -189,21 +191,46 @@ def chunk_prefill(q, k, v, g, b, cu_seqlens, chunk, pool, init_slot, final_slot,
     _same_device(q, (("k", k), ("v", v), ("g", g), ("b", b), ("o", o), ("pool", pool),
                      ("cu_seqlens", cu_seqlens), ("init_slot", init_slot), ("final_slot", final_slot),
                      ("track_ptr", track_ptr), ("track_chunk", track_chunk), ("track_slot", track_slot),
-                     ("track_f32", track_f32), ("dev_err", dev_err), ("workspace", workspace)))
+                     ("track_f32", track_f32), ("dev_err", dev_err),
+                     ("workspace", workspace if workspace is not False else None)))
     if o is None:
         o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
     _dev(o, "o", dtype=q.dtype)
-    need = prefill_workspace_bytes(n_seqs, T, H, dk, dv, chunk, q.dtype)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), DTYPE_CODES[q.dtype], _ptr(o),
+            _ptr(cu_seqlens), n_seqs, T, H, dk, dv, chunk, _pool(pool), _ptr(init_slot),
+            _ptr(final_slot), _ptr(track_ptr), _ptr(track_chunk), _ptr(track_slot), n_track,
+            _ptr(track_f32), QK_L2NORM if qk_l2norm else 0, _ptr(dev_err))
+    return o, args
+
+
+def chunk_prefill(q, k, v, g, b, cu_seqlens, chunk, pool, init_slot, final_slot,
+                  track_ptr=None, track_chunk=None, track_slot=None, track_f32=None,
+                  o=None, dev_err=None, workspace=None, qk_l2norm=False):
+    """kda_chunk_prefill on packed token tensors q, k, g [T, H, d_k], v [T, H, d_v],
+    b [T, H]; returns o [T, H, d_v] (allocated when not given).  qk_l2norm sets
+    KDA_QK_L2NORM (q and k normalised inside the kernel)."""
+    o, args = _prefill_marshal(q, k, v, g, b, cu_seqlens, chunk, pool, init_slot, final_slot, track_ptr,
+                               track_chunk, track_slot, track_f32, o, dev_err, workspace, qk_l2norm)
+    T, H, dk = q.shape
+    need = prefill_workspace_bytes(cu_seqlens.numel() - 1, T, H, dk, v.shape[2], chunk, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _dev(workspace, "workspace", dtype=torch.uint8)
-    st = lib().kda_chunk_prefill(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), DTYPE_CODES[q.dtype], _ptr(o),
-        _ptr(cu_seqlens), n_seqs, T, H, dk, dv, chunk, _pool(pool), _ptr(init_slot),
-        _ptr(final_slot), _ptr(track_ptr), _ptr(track_chunk), _ptr(track_slot), n_track,
-        _ptr(track_f32), QK_L2NORM if qk_l2norm else 0, _ptr(dev_err), _ptr(workspace),
-        workspace.numel(), _stream())
+    st = lib().kda_chunk_prefill(*args, _ptr(workspace), workspace.numel(), _stream())
     _check(st, "kda_chunk_prefill")
+    return o
+
+
+def chunk_prefill_noalloc(q, k, v, g, b, cu_seqlens, chunk, pool, init_slot, final_slot,
+                          track_ptr=None, track_chunk=None, track_slot=None, track_f32=None,
+                          o=None, dev_err=None, qk_l2norm=False):
+    """kda_chunk_prefill_noalloc: chunk_prefill without a workspace (the
+    library's static scratch of NOALLOC_SCRATCH_BYTES per GPU holds the chunk
+    records).  With ``o`` given, nothing is allocated."""
+    o, args = _prefill_marshal(q, k, v, g, b, cu_seqlens, chunk, pool, init_slot, final_slot, track_ptr,
+                               track_chunk, track_slot, track_f32, o, dev_err, False, qk_l2norm)
+    st = lib().kda_chunk_prefill_noalloc(*args, _stream())
+    _check(st, "kda_chunk_prefill_noalloc")
     return o
 
 

@@ -19,7 +19,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkda.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "prefill.hip", "prefill16.hip", "verify.hip", "commit.hip", "copy.hip", "conv.hip"]
+SOURCES = ["api.cpp", "prefill.hip", "prefill16.hip", "verify.hip", "commit.hip", "copy.hip", "conv.hip",
+           "noalloc.hip"]
 
 # Packed-fp32 VALU instructions are disabled for every device pass.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

@@ -60,15 +60,19 @@ kda_status kda_chunk_prefill_workspace(int32_t n_seqs, int64_t total_tokens, int
   return KDA_OK;
 }
 
-kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const void* g,
-                             const void* b, int32_t in_dtype, void* o,
-                             const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens,
-                             int32_t H, int32_t d_k, int32_t d_v, int32_t chunk, kda_pool pool,
-                             const int32_t* init_slot, const int32_t* final_slot,
-                             const int32_t* track_ptr, const int32_t* track_chunk,
-                             const int32_t* track_slot, int32_t n_track, float* track_f32,
-                             uint32_t flags, int32_t* dev_err, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Every host-side check of a prefill call except the workspace's; *need
+// receives the workspace bytes the call takes.  KDA_OK with n_seqs == 0
+// means there is nothing to do.
+kda_status prefill_check(const void* q, const void* k, const void* v, const void* g, const void* b,
+                         int32_t in_dtype, const void* o, const int32_t* cu_seqlens, int32_t n_seqs,
+                         int64_t total_tokens, int32_t H, int32_t d_k, int32_t d_v, int32_t chunk,
+                         const kda_pool& pool, const int32_t* init_slot, const int32_t* final_slot,
+                         const int32_t* track_ptr, const int32_t* track_chunk, const int32_t* track_slot,
+                         int32_t n_track, const float* track_f32, uint32_t flags, size_t* need) {
   if (n_seqs < 0 || total_tokens < 0 || H <= 0 || n_track < 0) return KDA_ERR_INVALID_ARG;
   if ((flags & ~KDA_QK_L2NORM) != 0) return KDA_ERR_INVALID_ARG;
   if (!dtype_ok(in_dtype)) return KDA_ERR_UNSUPPORTED;
@@ -87,14 +91,69 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(g, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(track_f32, 16))
     return KDA_ERR_INVALID_ARG;
-  const size_t need = kda::prefill_workspace_bytes(n_seqs, total_tokens, H, d_k, d_v, chunk, in_dtype);
-  if (workspace == nullptr || workspace_bytes < need) return KDA_ERR_WORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_WORKSPACE;
+  *need = kda::prefill_workspace_bytes(n_seqs, total_tokens, H, d_k, d_v, chunk, in_dtype);
+  return KDA_OK;
+}
+
+kda_status prefill_launch(const void* q, const void* k, const void* v, const void* g, const void* b,
+                          int32_t in_dtype, void* o, const int32_t* cu_seqlens, int32_t n_seqs,
+                          int64_t total_tokens, int32_t H, int32_t d_k, int32_t d_v, int32_t chunk,
+                          const kda_pool& pool, const int32_t* init_slot, const int32_t* final_slot,
+                          const int32_t* track_ptr, const int32_t* track_chunk, const int32_t* track_slot,
+                          int32_t n_track, float* track_f32, uint32_t flags, int32_t* dev_err,
+                          void* workspace, void* stream) {
   kda::PrefillArgs a{q, k, v, g, b, o, in_dtype, cu_seqlens, n_seqs, total_tokens, H, d_k, d_v,
                      chunk, pool_desc(pool), init_slot, final_slot,
                      n_track > 0 ? track_ptr : nullptr, track_chunk, track_slot, n_track,
                      track_f32, dev_err, workspace, flags};
   return launched(kda::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const void* g,
+                             const void* b, int32_t in_dtype, void* o,
+                             const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens,
+                             int32_t H, int32_t d_k, int32_t d_v, int32_t chunk, kda_pool pool,
+                             const int32_t* init_slot, const int32_t* final_slot,
+                             const int32_t* track_ptr, const int32_t* track_chunk,
+                             const int32_t* track_slot, int32_t n_track, float* track_f32,
+                             uint32_t flags, int32_t* dev_err, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  kda_status s = prefill_check(q, k, v, g, b, in_dtype, o, cu_seqlens, n_seqs, total_tokens, H, d_k, d_v,
+                               chunk, pool, init_slot, final_slot, track_ptr, track_chunk, track_slot,
+                               n_track, track_f32, flags, &need);
+  if (s != KDA_OK || n_seqs == 0) return s;
+  if (workspace == nullptr || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_WORKSPACE;
+  return prefill_launch(q, k, v, g, b, in_dtype, o, cu_seqlens, n_seqs, total_tokens, H, d_k, d_v, chunk,
+                        pool, init_slot, final_slot, track_ptr, track_chunk, track_slot, n_track, track_f32,
+                        flags, dev_err, workspace, stream);
+}
+
+kda_status kda_chunk_prefill_noalloc(const void* q, const void* k, const void* v, const void* g,
+                                     const void* b, int32_t in_dtype, void* o,
+                                     const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens,
+                                     int32_t H, int32_t d_k, int32_t d_v, int32_t chunk, kda_pool pool,
+                                     const int32_t* init_slot, const int32_t* final_slot,
+                                     const int32_t* track_ptr, const int32_t* track_chunk,
+                                     const int32_t* track_slot, int32_t n_track, float* track_f32,
+                                     uint32_t flags, int32_t* dev_err, void* stream) {
+  size_t need = 0;
+  kda_status s = prefill_check(q, k, v, g, b, in_dtype, o, cu_seqlens, n_seqs, total_tokens, H, d_k, d_v,
+                               chunk, pool, init_slot, final_slot, track_ptr, track_chunk, track_slot,
+                               n_track, track_f32, flags, &need);
+  if (s != KDA_OK || n_seqs == 0) return s;
+  if (need > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE;
+  // the library's static scratch on the current device: its address, never the array's name
+  void* ws = nullptr;
+  if (kda::noalloc_scratch(&ws) != hipSuccess) return KDA_ERR_LAUNCH;
+  return prefill_launch(q, k, v, g, b, in_dtype, o, cu_seqlens, n_seqs, total_tokens, H, d_k, d_v, chunk,
+                        pool, init_slot, final_slot, track_ptr, track_chunk, track_slot, n_track, track_f32,
+                        flags, dev_err, ws, stream);
 }
 
 kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, const void* g,
@@ -182,6 +241,7 @@ kda_status kda_state_copy(kda_pool pool, const int32_t* src_slot, const int32_t*
 }
 
 static_assert(KDA_MAX_CONV_TENSORS == kda::kMaxConvTensors, "conv tensor limit");
+static_assert(KDA_NOALLOC_SCRATCH_BYTES == kda::kNoallocScratchBytes, "static scratch size");
 
 kda_status kda_conv_state_update(const kda_conv_tensor* tensors, int32_t n_tensors,
                                  const int32_t* dst_slot, const int32_t* src_slot,

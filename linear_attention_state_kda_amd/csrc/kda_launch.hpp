@@ -101,6 +101,12 @@ struct ConvArgs {
   int32_t* dev_err;
 };
 
+// Static scratch of the allocation-free prefill entry point (noalloc.hip):
+// its size, and its device address on the current device (resolved once per
+// device, then cached).
+constexpr size_t kNoallocScratchBytes = (size_t)256 << 20;
+hipError_t noalloc_scratch(void** out);
+
 // Shape support and sizes.
 bool prefill_supported(int dk, int dv, int chunk, int in_dtype, int pool_dtype);
 size_t prefill_workspace_bytes(int n_seqs, int64_t total_tokens, int H, int dk, int dv,

@@ -53,6 +53,18 @@ int main(void) {
                                                      64, pool, fi, fi, NULL, NULL, NULL, 0, NULL, 0u, NULL, fake_ws,
                                                      (size_t)1 << 40, NULL), KDA_ERR_INVALID_ARG);
   }
+  expect("noalloc pool H", kda_chunk_prefill_noalloc(fake, fake, fake, fake, fake, KDA_BF16, fake, fi, 2, 2 * 8229, 3,
+                                                     128, 128, 64, pool, fi, fi, NULL, NULL, NULL, 0, NULL, 0u,
+                                                     NULL, NULL), KDA_ERR_INVALID_ARG);   /* pool H = 2, call H = 3 */
+  {
+    kda_pool p32 = {fake, 8, KDA_F32, 32, 128, 128};
+    expect("noalloc over the scratch", kda_chunk_prefill_noalloc(fake, fake, fake, fake, fake, KDA_BF16, fake, fi, 2,
+                                                                 2 * 8229, 32, 128, 128, 64, p32, fi, fi, NULL, NULL,
+                                                                 NULL, 0, NULL, 0u, NULL, NULL), KDA_ERR_WORKSPACE);
+  }
+  expect("noalloc nothing to do", kda_chunk_prefill_noalloc(NULL, fake, fake, fake, fake, KDA_BF16, fake, NULL, 0, 0, 2,
+                                                            128, 128, 64, pool, NULL, NULL, NULL, NULL, NULL, 0, NULL,
+                                                            0u, NULL, NULL), KDA_OK);
   expect("prefill nothing to do", PREFILL(NULL, 0, 128, 64, KDA_BF16, KDA_QK_L2NORM, 0), KDA_OK);
 #undef PREFILL
 

@@ -184,3 +184,27 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(kda, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(kda.KdaError):
         kda.lib()
+
+
+def test_prefill_noalloc_host_errors(L):
+    """The allocation-free prefill: the same host checks as kda_chunk_prefill,
+    and a call whose workspace would exceed the static scratch is rejected
+    before any launch (so no device is touched here)."""
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, in_dtype=2, o=FAKE, cu=FAKE, n_seqs=1,
+                 T=100, H=2, dk=128, dv=128, C=64, pool=pool(), init=FAKE, final=FAKE, tptr=None,
+                 tchunk=None, tslot=None, n_track=0, tf32=None, flags=0, err=None, stream=None)
+        a.update(kw)
+        return L.kda_chunk_prefill_noalloc(*a.values())
+    assert call(q=None) == 1
+    assert call(C=32) == 2
+    assert call(v=ctypes.c_void_p(0x1008)) == 1
+    assert call(n_seqs=0, q=None, cu=None) == 0
+    out = ctypes.c_size_t(0)
+    # 2 x 8229 tokens at 32 heads need about 460 MB of records: more than the 256 MiB scratch
+    assert L.kda_chunk_prefill_workspace(2, 2 * 8229, 32, 128, 128, 64, 2, ctypes.byref(out)) == 0
+    assert out.value > kda.NOALLOC_SCRATCH_BYTES
+    assert call(n_seqs=2, T=2 * 8229, H=32, pool=pool(H=32)) == 3
+    # the single-layer workload fits
+    assert L.kda_chunk_prefill_workspace(1, 8229, 32, 128, 128, 64, 2, ctypes.byref(out)) == 0
+    assert out.value <= kda.NOALLOC_SCRATCH_BYTES
