@@ -4,20 +4,29 @@ One step = one pass of the whole path over resident synthetic inputs:
   * kda_chunk_prefill on the single-layer workload (1 sequence, T = 8229 =
     128 full chunks + a tail of 37, H = 32 heads, d_k = d_v = 128, chunk 64,
     bf16 q/k/v/g/b, fp32 pool, zero initial state, snapshot at c = 128);
-  * kda_recurrent_verify, kda_commit and kda_state_copy on the speculative
-    workload (256 requests, L = 8, H = 32, fp32 128 x 128 checkpoints in a
-    1024-slot pool, accepted ~ U{0..8}, in-place commit, fork of 64
-    committed checkpoints to 4 children each).
-value = prefill tokens/s (T / mean prefill time).  Informational legs
-outside the step time the same prefill on the varlen batch (16 sequences,
-lengths ~ U[512, 16384]; `prefill_varlen`) and on one 131072-token sequence
-(`prefill_long`), and the verify -> commit -> fork copy loop of speculative
-decoding back to back (`decode_loop`).  Each call is bracketed by
-HIP events on the stream it is launched on; the roofline object covers the
-call that dominates the step.  The cpu_baseline leg times the fp64 oracle
-(single thread) on the first tokens of the same prefill workload.
+  * kda_recurrent_verify, kda_commit, kda_commit_align, kda_state_copy and
+    the conv-state update on the speculative workload (256 requests, L = 8,
+    H = 32, fp32 128 x 128 checkpoints in a 1024-slot pool, accepted
+    ~ U{0..8}, in-place commit, fork of 64 committed checkpoints to 4
+    children each).
+Two passes of K steps each: a warm pass back to back (bracketed by the wall
+clock: ms_per_step), and a flushed pass in which, before every step and
+outside its timed calls, the checkpoint slots the commits overwrite are
+restored from a pristine copy and a 512 MiB write evicts the L2 and the
+memory-side cache, so every call starts with its inputs in HBM only.
+value = prefill tokens/s = T / median flushed prefill time (the warm figure
+is reported beside it).  Each call is bracketed by HIP events on the stream
+it is launched on; the roofline object covers the call that dominates the
+step.  Informational legs outside the step time the same prefill on the
+varlen batch (16 sequences, lengths ~ U[512, 16384]; `prefill_varlen`) and
+on one 131072-token sequence (`prefill_long`), each with its own roofline
+fractions, and the verify -> commit -> fork copy loop of speculative
+decoding back to back (`decode_loop`).  The cpu_baseline leg times the fp64
+oracle on the host's cores (one process per group of heads), before the GPU
+is touched.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-varlen]
+       python bench.py --only-leg long|varlen   (one informational leg alone, for profiling)
 """
 
 import argparse
@@ -156,12 +165,14 @@ def informational_setup(dev, case):
     return args, T, len(lengths), bytes_, flops
 
 
-def time_leg(dev, st, case, label):
-    """Median of 5 prefill calls (after 2 untimed) on an informational workload."""
+def time_leg(dev, st, case, label, reps=5):
+    """Median of `reps` prefill calls (after 2 untimed) on an informational
+    workload, with its roofline fractions (HBM: algorithmic bytes; MFMA:
+    algorithmic FLOP against the dense bf16 peak)."""
     args, T, n, bytes_, flops = informational_setup(dev, case)
     for _ in range(2):
         kda.chunk_prefill(**args)
-    evs = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(5)]
+    evs = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(reps)]
     for e0, e1 in evs:
         e0.record(st)
         kda.chunk_prefill(**args)
@@ -169,10 +180,16 @@ def time_leg(dev, st, case, label):
     torch.cuda.synchronize()
     ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
     del args
+    s_ = ms * 1e-3
     return {"workload": f"{label}, {n} sequence(s), {T} tokens, H=32, d=128, chunk 64, bf16, fp32 pool",
-            "ms_median": ms, "tokens_per_s": T / (ms * 1e-3),
-            "hbm_GBps": bytes_ / (ms * 1e-3) / 1e9, "hbm_frac": bytes_ / (ms * 1e-3) / HBM_PEAK,
-            "mfma_TFLOPs": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / BF16_PEAK}
+            "ms_median": ms, "tokens_per_s": T / s_,
+            "hbm_GBps": bytes_ / s_ / 1e9, "hbm_frac": bytes_ / s_ / HBM_PEAK,
+            "mfma_TFLOPs": flops / s_ / 1e12, "mfma_frac": flops / s_ / BF16_PEAK,
+            "roofline": {"kernel": "kda_chunk_prefill (kda_chunk_map + kda_chunk_prep16 + kda_chunk_scan16)",
+                         "bound": "hbm", "achieved": bytes_ / s_ / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                         "frac": bytes_ / s_ / HBM_PEAK, "algorithmic_bytes_per_launch": bytes_,
+                         "algorithmic_flop_per_launch": flops, "mfma_frac": flops / s_ / BF16_PEAK,
+                         "avg_launch_ms": ms}}
 
 
 def decode_loop_leg(sp, st, iters=10, warm=3):
@@ -208,7 +225,8 @@ def decode_loop_leg(sp, st, iters=10, warm=3):
 def measured_prefill_traffic():
     """HBM bytes per prefill call from the committed FETCH_SIZE / WRITE_SIZE
     profile (already scaled by the copy calibration), or None when the
-    prefill sources changed since those counters were taken."""
+    prefill sources changed since those counters were taken; with a label
+    naming where the figure comes from."""
     import hashlib
     h = hashlib.sha256()
     for name in ("prefill.hip", "prefill16.hip", "prefill_common.hpp", "kda_common.hpp", "kda_launch.hpp"):
@@ -218,10 +236,14 @@ def measured_prefill_traffic():
         fields = dict(line.split(": ", 1) for line in open(TRAFFIC_PROFILE).read().splitlines()
                       if line.startswith(("traffic_bytes_per_call: ", "source_sha256_16: ")))
     except OSError:
-        return None
+        return None, "none: profiles/prefill_traffic.md missing"
     if fields.get("source_sha256_16", "").strip() != h.hexdigest()[:16]:
-        return None
-    return int(fields["traffic_bytes_per_call"])
+        return None, f"none: the prefill sources (sha256 {h.hexdigest()[:16]}) changed since the counters in " \
+                     f"profiles/prefill_traffic.md were taken"
+    return int(fields["traffic_bytes_per_call"]), \
+        f"profiles/prefill_traffic.md: rocprofv3 FETCH_SIZE and WRITE_SIZE of the same kernels, scaled by a " \
+        f"plain copy of known size, taken for prefill sources sha256 {h.hexdigest()[:16]} (the ones built " \
+        f"here); not measured in this run"
 
 
 def cpu_model():
@@ -235,26 +257,48 @@ def cpu_model():
     return platform.processor() or platform.machine()
 
 
-def cpu_baseline(case, seconds_target=20.0):
-    """Time the fp64 oracle, single thread, on the first tokens of the prefill."""
+def _oracle_heads(args):
+    """Worker of the CPU baseline: the fp64 token loop on a group of heads
+    of the first n tokens (one thread per process)."""
+    case, heads, n = args
     from threadpoolctl import threadpool_limits
     from oracle import kda_oracle as ko
 
-    toks, _ = wl.prefill_tokens(case)
-    H, d = case["H"], case["dk"]
-    ex = {n: wl.exact(toks[n]) for n in "qkvgb"}
+    d = case["dk"]
+    toks = wl.token_inputs(case["lengths"][0], case["H"], d, d, case["in_dtype"], case["seed"], heads=heads)
+    ex = {x: wl.exact(toks[x][:n]) for x in "qkvgb"}
     with threadpool_limits(limits=1):
-        n = 64
+        ko.run_sequence(*(ex[x][:8] for x in "qkvgb"), np.zeros((len(heads), d, d)))   # first-call costs
         t0 = time.perf_counter()
-        ko.run_sequence(*(ex[x][:n] for x in "qkvgb"), np.zeros((H, d, d)))
-        per_tok = (time.perf_counter() - t0) / n
-        n2 = int(max(256, min(case["lengths"][0], seconds_target / per_tok)))
+        ko.run_sequence(*(ex[x] for x in "qkvgb"), np.zeros((len(heads), d, d)))
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(case, seconds_target=20.0):
+    """Time the fp64 oracle on the host's cores: the heads are independent,
+    so one process per group of heads runs the token loop over the same
+    first tokens; the wall time of the slowest group gives tokens/s.  Runs
+    before the GPU is initialised (worker processes are spawned, never
+    forked from a process holding the GPU)."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    H = case["H"]
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16, H))
+    groups = [list(range(H))[i::cores] for i in range(cores)]
+    ctx = mp.get_context("spawn")
+    with cf.ProcessPoolExecutor(max_workers=cores, mp_context=ctx) as ex:
+        # a short probe sizes the sample to about `seconds_target` of wall time
+        probe = 64
+        t_probe = max(ex.map(_oracle_heads, [(case, g, probe) for g in groups]))
+        n = int(max(256, min(case["lengths"][0], probe * seconds_target / max(t_probe, 1e-6))))
         t0 = time.perf_counter()
-        ko.run_sequence(*(ex[x][:n2] for x in "qkvgb"), np.zeros((H, d, d)))
-        dt = time.perf_counter() - t0
-    return {"value": n2 / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n2} of {case['lengths'][0]} tokens of the single-layer prefill, all "
-                      f"{H} heads, fp64 token loop ({dt:.1f} s)"}
+        worst = max(ex.map(_oracle_heads, [(case, g, n) for g in groups]))
+        wall = time.perf_counter() - t0
+    return {"value": n / worst, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n} of {case['lengths'][0]} tokens of the single-layer prefill, all {H} heads "
+                      f"in {cores} processes of {H // cores}-{-(-H // cores)} heads each, fp64 token loop "
+                      f"(slowest process {worst:.1f} s, {wall:.1f} s wall with input setup)"}
 
 
 def main():
@@ -263,12 +307,14 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold-steps", type=int, default=10,
-                    help="extra steps, each after a 512 MiB cache-flushing write (0 to skip)")
+    ap.add_argument("--cold-steps", type=int, default=None,
+                    help="steps of the flushed pass (default: --steps; value is taken from this pass)")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the informational legs (prefill on the varlen batch of 16 "
                          "sequences and on the long-context sequence of 131072 tokens; the "
                          "speculative-decoding loop)")
+    ap.add_argument("--only-leg", choices=("long", "varlen"), default=None,
+                    help="run one informational prefill leg alone (10 timed calls) and print it")
     ap.add_argument("--traffic-calibration", action="store_true",
                     help="after the timed steps, run one kda_state_copy of 256 distinct fp32 "
                          "slots (512 MiB read + 512 MiB written) so that FETCH_SIZE / WRITE_SIZE "
@@ -278,11 +324,24 @@ def main():
         print("bench.py measures one GPU: the KDA path here is built and timed on a single "
               "MI355X (no collectives); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    cold_steps = a.steps if a.cold_steps is None else a.cold_steps
+    case = wl.single_layer_prefill()
+    # the oracle baseline runs first, on the host's cores, before anything touches the GPU
+    cb = None
+    if not a.no_cpu_baseline and a.only_leg is None:
+        cb = cpu_baseline(case)
+        cb["cpu"] = cpu_model()
     dev = torch.device("cuda:0")
     kda.lib()
+    st = torch.cuda.current_stream()
+    if a.only_leg is not None:
+        leg = wl.long_prefill() if a.only_leg == "long" else wl.varlen_prefill("f32")
+        print(json.dumps({"leg": a.only_leg, **time_leg(dev, st, leg, a.only_leg, reps=10)}), flush=True)
+        return
     case, pargs, T, p_bytes, p_flops = prefill_setup(dev)
     sp = spec_setup(dev)
-    st = torch.cuda.current_stream()
+    ck_long = sp["ckpt"].long()
+    pristine = sp["pool"][ck_long].clone()    # the checkpoints, before any commit
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
@@ -315,6 +374,7 @@ def main():
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
+    # ---- warm pass: K steps back to back, wall-clock bracketed
     evs = [[ev() for _ in range(len(calls) + 1)] for _ in range(a.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -326,18 +386,19 @@ def main():
            for i, c in enumerate(calls)}
     ms = {c: float(per[c].mean()) for c in calls}
     ms_step = wall / a.steps * 1e3
-    # Second pass, not part of `value`: a 512 MiB scratch write between steps
-    # (outside the per-call events) evicts L2 and the MALL, so every call
-    # starts with its inputs in HBM only.
+    # ---- flushed pass: before every step, outside its timed calls, the
+    #      checkpoints the commits overwrite are restored and a 512 MiB write
+    #      evicts L2 and the MALL
     cold = None
-    if a.cold_steps > 0:
+    if cold_steps > 0:
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        cevs = [[ev() for _ in range(len(calls) + 1)] for _ in range(a.cold_steps)]
-        for s in range(a.cold_steps):
+        cevs = [[ev() for _ in range(len(calls) + 1)] for _ in range(cold_steps)]
+        for s in range(cold_steps):
+            sp["pool"].index_copy_(0, ck_long, pristine)
             scratch.fill_(s & 0xFF)
             step(cevs[s])
         torch.cuda.synchronize()
-        cold = {c: np.array([cevs[s][i].elapsed_time(cevs[s][i + 1]) for s in range(a.cold_steps)])
+        cold = {c: np.array([cevs[s][i].elapsed_time(cevs[s][i + 1]) for s in range(cold_steps)])
                 for i, c in enumerate(calls)}
         del scratch
     # Informational legs, outside the step and `value`: the same prefill
@@ -380,23 +441,33 @@ def main():
         return {"median": float(np.median(x)), "p10": float(np.percentile(x, 10)),
                 "p90": float(np.percentile(x, 90))}
 
-    p_s = ms["prefill"] * 1e-3
+    # value and the per-call figures: the flushed pass's medians (the warm
+    # pass's means beside them)
+    sel = {c: (float(np.median(cold[c])) if cold is not None else ms[c]) for c in calls}
+    basis = ("median of %d flushed steps (L2 and MALL evicted and checkpoints restored before each "
+             "step, outside the timed calls)" % cold_steps) if cold is not None else \
+        "mean of %d warm steps" % a.steps
+    p_s = sel["prefill"] * 1e-3
     tokens_per_s = T / p_s
     state_calls = ("verify", "commit", "commit_align", "conv_compact", "copy", "conv_fork")
-    gbs = {c: sp["bytes"][c] / (ms[c] * 1e-3) / 1e9 for c in state_calls}
-    dominant = max(calls, key=lambda c: ms[c])
+    gbs = {c: sp["bytes"][c] / (sel[c] * 1e-3) / 1e9 for c in state_calls}
+    dominant = max(calls, key=lambda c: sel[c])
     if dominant == "prefill":
         achieved = p_bytes / p_s / 1e9
+        traffic, traffic_src = measured_prefill_traffic()
         roof = {"kernel": "kda_chunk_prefill (kda_chunk_map + kda_chunk_prep16 + kda_chunk_scan16)",
                 "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                "frac": achieved * 1e9 / HBM_PEAK, "traffic": measured_prefill_traffic(),
-                "algorithmic_bytes_per_launch": p_bytes, "avg_launch_ms": ms["prefill"]}
+                "frac": achieved * 1e9 / HBM_PEAK, "traffic": traffic, "traffic_source": traffic_src,
+                "algorithmic_bytes_per_launch": p_bytes, "algorithmic_flop_per_launch": p_flops,
+                "mfma_frac": p_flops / p_s / BF16_PEAK, "avg_launch_ms": sel["prefill"],
+                "timing": basis}
     else:
         achieved = gbs[dominant]
         roof = {"kernel": f"kda_{dominant}", "bound": "hbm", "achieved": achieved,
                 "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": achieved * 1e9 / HBM_PEAK,
-                "traffic": None, "algorithmic_bytes_per_launch": sp["bytes"][dominant],
-                "avg_launch_ms": ms[dominant]}
+                "traffic": None, "traffic_source": "none: not taken for this kernel",
+                "algorithmic_bytes_per_launch": sp["bytes"][dominant], "avg_launch_ms": sel[dominant],
+                "timing": basis}
     out = {
         "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True,
@@ -406,27 +477,27 @@ def main():
                                "+ align-mode commit (64-token blocks) + conv-state compaction/fork "
                                "(3 x 4096 channels, width 4, bf16)",
                    "global_batch": 1, "seq_len": T, "heads": 32, "head_dim": 128, "chunk": 64},
-        "prefill": {"ms": ms["prefill"], "ms_spread": spread(per["prefill"]), "tokens_per_s": tokens_per_s,
+        "value_basis": "prefill tokens/s, T / " + basis,
+        "prefill": {"ms": sel["prefill"], "ms_warm_mean": ms["prefill"], "ms_warm_spread": spread(per["prefill"]),
+                    "tokens_per_s": tokens_per_s, "tokens_per_s_warm": T / (ms["prefill"] * 1e-3),
                     "hbm_GBps": p_bytes / p_s / 1e9, "hbm_frac": p_bytes / p_s / HBM_PEAK,
                     "mfma_TFLOPs": p_flops / p_s / 1e12, "mfma_frac": p_flops / p_s / BF16_PEAK},
-        **{c: {"ms": ms[c], "ms_spread": spread(per[c]), "GBps": gbs[c], "hbm_frac": gbs[c] * 1e9 / HBM_PEAK}
-           for c in state_calls},
+        **{c: {"ms": sel[c], "ms_warm_mean": ms[c], "ms_warm_spread": spread(per[c]), "GBps": gbs[c],
+               "hbm_frac": gbs[c] * 1e9 / HBM_PEAK,
+               "hbm_frac_warm": sp["bytes"][c] / (ms[c] * 1e-3) / HBM_PEAK} for c in state_calls},
         "roofline": roof,
         "hbm_reference": hbm_reference,
         "cold": None if cold is None else {
-            "note": "L2 and MALL flushed by a 512 MiB write before each step",
-            "steps": a.cold_steps,
+            "note": "L2 and MALL flushed by a 512 MiB write and the checkpoints restored before each step",
+            "steps": cold_steps,
             **{c: {"ms_median": float(np.median(cold[c])), "ms_p10": float(np.percentile(cold[c], 10)),
-                   "ms_p90": float(np.percentile(cold[c], 90))} for c in calls},
-            "prefill_tokens_per_s": T / (float(np.median(cold["prefill"])) * 1e-3)},
+                   "ms_p90": float(np.percentile(cold[c], 90))} for c in calls}},
         "prefill_varlen": varlen,
         "prefill_long": long_ctx,
         "decode_loop": loop,
         "device": torch.cuda.get_device_name(0),
     }
-    if not a.no_cpu_baseline:
-        cb = cpu_baseline(case)
-        cb["cpu"] = cpu_model()
+    if cb is not None:
         out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 

@@ -291,10 +291,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   //      leaves the fp32 range, below about -88, for bf16, at |k| <= 1) is
   //      flagged with the gate-range error bit instead of passing silently.
   F8 ktf[NFK], qtf[NFK], kbf[NFK], khf[NFK];
-  // smallest fp32 magnitude that rounds to infinity in T (RNE): halfway
-  // between T's largest finite value and the next power of two
-  constexpr float kInf16 = std::is_same<T, f16>::value ? 65520.f : __builtin_bit_cast(float, 0x7F7F8000u);
-  bool range_ok = true;
 #pragma unroll
   for (int kb = 0; kb < NFK; ++kb)
 #pragma unroll
@@ -310,15 +306,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
         const float kv = to_f32(kr[kb][hf][e]);
         const float qv = to_f32(qr[kb][hf][e]);
         const float kbv = kv * b;
-        const float khv = kbv * ni[e];
-        range_ok = range_ok && __builtin_fabsf(khv) < kInf16;   // false for inf and NaN too
         ktf[kb][4 * hf + e] = from_f32<T>(kv * a);
         qtf[kb][4 * hf + e] = from_f32<T>(qv * a);
         kbf[kb][4 * hf + e] = from_f32<T>(kbv);
-        khf[kb][4 * hf + e] = from_f32<T>(khv);
+        khf[kb][4 * hf + e] = from_f32<T>(kbv * ni[e]);
       }
     }
-  if (__builtin_amdgcn_ballot_w64(!range_ok) != 0 && lane == 0) set_err(dev_err, 1u << 5);
   // Records are stored non-temporally, in whole 16-byte fragment pieces
   // (Z and Pw are assembled in LDS first): the scan reads each record once,
   // about a prep's duration later, and dirty records left in the
@@ -334,6 +327,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
                                 reinterpret_cast<u32x4*>(rec + R::kQt + (w * NFK + kb) * kFB + lane * 16));
     sm.r1.kh[w][kb][lane] = __builtin_bit_cast(uint4, khf[kb]);
   }
+
   // 0/1 selection fragments: sel[hf] picks channel 16 hf + r of a K-block, so
   // the product X sel[hf] is the transpose of X's 16 x 16 tile hf, in the
   // accumulator layout (token rows 4g + e, channel column r): half (w % 2)
@@ -359,6 +353,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   //      then holds P[16w + r][16jt + 4g + e], the row form of P_w,jt.
   floatx4 ptile[4], nrow[4];
   const int rr = 16 * w + r;  // this lane's row of P, M, N, T
+  // Wave 3 reads every Kh tile: an element whose exponent field is all ones
+  // rounded to infinity (or is NaN), so the chunk is beyond the supported
+  // gate range
+  constexpr uint32_t kExp = std::is_same<T, f16>::value ? 0x7C00u : 0x7F80u, kExp2 = kExp << 16;
+  uint32_t kh_bad = 0;
 #pragma unroll
   for (int jt = 0; jt < 4; ++jt) {
     ptile[jt] = nrow[jt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -366,9 +365,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     floatx4 pm = {0.f, 0.f, 0.f, 0.f}, pp = pm;
 #pragma unroll
     for (int kb = 0; kb < NFK; ++kb) {
-      const F8 a = __builtin_bit_cast(F8, sm.r1.kh[jt][kb][lane]);
+      const uint4 araw = sm.r1.kh[jt][kb][lane];
+      const F8 a = __builtin_bit_cast(F8, araw);
       pm = mma(pm, a, ktf[kb]);
       pp = mma(pp, a, qtf[kb]);
+      if (w == 3)
+        for (uint32_t wd : {araw.x, araw.y, araw.z, araw.w}) kh_bad |= ((wd & kExp) == kExp) | ((wd & kExp2) == kExp2);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -377,6 +379,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
       nrow[jt][e] = s < rr ? beta * pm[e] : 0.f;
     }
   }
+  if (w == 3 && __builtin_amdgcn_ballot_w64(kh_bad != 0) != 0 && lane == 0) set_err(dev_err, 1u << 5);
   // P fragments: block (w, b) = [P_w,2b | P_w,2b+1] for token blocks b up to the diagonal
 #pragma unroll
   for (int b = 0; b < 2; ++b)

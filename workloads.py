@@ -54,25 +54,30 @@ def _unit_rows(x):
     return x / np.linalg.norm(x, axis=-1, keepdims=True)
 
 
-def token_inputs(n_tokens, H, dk, dv, in_dtype, seed, shape_prefix=None):
+def token_inputs(n_tokens, H, dk, dv, in_dtype, seed, shape_prefix=None, heads=None):
     """Draw q, k, v, g, b for ``n_tokens`` token rows of H heads.
 
     Returns a dict of CPU torch tensors in ``in_dtype``.  ``shape_prefix``
     reshapes the leading token axis (e.g. (n_req, L) for the spec layout).
+    ``heads`` draws only those heads (the head axis then follows that
+    list): each head has its own streams, so the values are the same as in
+    the full draw.
     """
     T = int(n_tokens)
     dt = DTYPES[in_dtype]
-    q = torch.empty((T, H, dk), dtype=dt)
-    k = torch.empty((T, H, dk), dtype=dt)
-    v = torch.empty((T, H, dv), dtype=dt)
-    g = torch.empty((T, H, dk), dtype=dt)
-    b = torch.empty((T, H), dtype=dt)
-    for h in range(H):
-        q[:, h] = to_dtype(_unit_rows(_rng(seed, TAG_Q, h).standard_normal((T, dk))), in_dtype)
-        k[:, h] = to_dtype(_unit_rows(_rng(seed, TAG_K, h).standard_normal((T, dk))), in_dtype)
-        v[:, h] = to_dtype(_rng(seed, TAG_V, h).standard_normal((T, dv)), in_dtype)
-        b[:, h] = to_dtype(_rng(seed, TAG_B, h).standard_normal(T), in_dtype)
-        g[:, h] = to_dtype(_rng(seed, TAG_G, h).uniform(G_LO, G_HI, (T, dk)), in_dtype)
+    hs = list(range(H)) if heads is None else [int(x) for x in heads]
+    n_h = len(hs)
+    q = torch.empty((T, n_h, dk), dtype=dt)
+    k = torch.empty((T, n_h, dk), dtype=dt)
+    v = torch.empty((T, n_h, dv), dtype=dt)
+    g = torch.empty((T, n_h, dk), dtype=dt)
+    b = torch.empty((T, n_h), dtype=dt)
+    for j, h in enumerate(hs):
+        q[:, j] = to_dtype(_unit_rows(_rng(seed, TAG_Q, h).standard_normal((T, dk))), in_dtype)
+        k[:, j] = to_dtype(_unit_rows(_rng(seed, TAG_K, h).standard_normal((T, dk))), in_dtype)
+        v[:, j] = to_dtype(_rng(seed, TAG_V, h).standard_normal((T, dv)), in_dtype)
+        b[:, j] = to_dtype(_rng(seed, TAG_B, h).standard_normal(T), in_dtype)
+        g[:, j] = to_dtype(_rng(seed, TAG_G, h).uniform(G_LO, G_HI, (T, dk)), in_dtype)
     out = {"q": q, "k": k, "v": v, "g": g, "b": b}
     if shape_prefix is not None:
         pre = tuple(int(x) for x in shape_prefix)
