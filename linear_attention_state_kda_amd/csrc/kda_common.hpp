@@ -2,13 +2,10 @@
 //
 // * Scalar types and round-to-nearest-even casts (bf16/fp16 casts lower to
 //   the hardware's RNE convert instructions).
-// * 16x16 MFMA tiles with fp32 accumulation.  A "fragment" is what one lane
-//   feeds into a 16 x 16 x KB product: KB/4 consecutive elements of a K-block
-//   stored in a permuted order (see pos_in_block).  Because the same
-//   permutation is used for both operands, any permutation gives the plain
-//   contraction; the one chosen here makes the fp32 accumulator tile of one
-//   product (lane l holds column l%16, rows 4*(l/16)+i) directly usable as the
-//   B fragment of the next product, with no data movement.
+// * 16x16 MFMA tiles with fp32 accumulation: the 16-bit products
+//   (16x16x32, used by the 16-bit prefill, which lays out its own fragments)
+//   and the fp32 fragments of the general chunk form (16x16x4 over K-blocks
+//   of 16, one 16-byte fragment per lane).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -67,27 +64,12 @@ __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __ex
 
 // ---------------------------------------------------------------- fragments
 
-// K-block size used by an operand type: 32 for the 16-bit 16x16x32 MFMAs,
-// any multiple of 4 (16 or 32 here) for fp32 16x16x4.
+// 8 x 16-bit fragment type of the 16x16x32 MFMAs.
 template <typename TOp> struct OpTraits;
-template <> struct OpTraits<bf16> { static constexpr int KB = 32; typedef bf16x8 frag; };
-template <> struct OpTraits<f16> { static constexpr int KB = 32; typedef f16x8 frag; };
+template <> struct OpTraits<bf16> { typedef bf16x8 frag; };
+template <> struct OpTraits<f16> { typedef f16x8 frag; };
 
 template <int N> struct f32frag { float v[N]; };
-
-// Storage position of index `idx` (0 <= idx < KB) inside a K-block.
-// KB == 32: lane group g (lanes 16g..16g+15) owns positions 8g..8g+7 which
-// hold indices {4g..4g+3} and {16+4g..16+4g+3}; KB == 16: identity.
-template <int KB>
-__host__ __device__ constexpr int pos_in_block(int idx) {
-  return KB == 16 ? idx
-                  : (idx < 16 ? ((idx >> 2) << 3) + (idx & 3)
-                              : (((idx - 16) >> 2) << 3) + 4 + (idx & 3));
-}
-template <int KB>
-__host__ __device__ constexpr int pos_of(int idx) {
-  return (idx / KB) * KB + pos_in_block<KB>(idx % KB);
-}
 
 // 16x16 MFMA products, fp32 accumulate.
 __device__ __forceinline__ floatx4 mma(floatx4 c, bf16x8 a, bf16x8 b) {
@@ -103,70 +85,18 @@ __device__ __forceinline__ floatx4 mma(floatx4 c, const f32frag<N>& a, const f32
   return c;
 }
 
-// Fragment loads from a K-contiguous row (row pointer already offset to the
-// lane's row).  kb = K-block index, g = lane / 16.
-template <typename TOp, int KB> struct Frag;
-template <> struct Frag<bf16, 32> {
-  typedef bf16x8 type;
-  __device__ __forceinline__ static type load(const bf16* row, int kb, int g) {
-    return *reinterpret_cast<const bf16x8*>(row + kb * 32 + 8 * g);
-  }
-};
-template <> struct Frag<f16, 32> {
-  typedef f16x8 type;
-  __device__ __forceinline__ static type load(const f16* row, int kb, int g) {
-    return *reinterpret_cast<const f16x8*>(row + kb * 32 + 8 * g);
-  }
-};
-template <int KB> struct Frag<float, KB> {
-  typedef f32frag<KB / 4> type;
-  __device__ __forceinline__ static type load(const float* row, int kb, int g) {
-    type f;
-    const float* p = row + kb * KB + (KB / 4) * g;
-#pragma unroll
-    for (int j = 0; j < KB / 4; j += 4) {
-      floatx4 x = *reinterpret_cast<const floatx4*>(p + j);
-      f.v[j] = x[0]; f.v[j + 1] = x[1]; f.v[j + 2] = x[2]; f.v[j + 3] = x[3];
-    }
-    return f;
-  }
-};
-
-// B fragment built from accumulator tiles held in registers: the K-block
-// covers two consecutive 16-row tiles (KB == 32) or one (KB == 16).
-template <typename TOp, int KB> struct RegFrag;
-template <> struct RegFrag<bf16, 32> {
-  __device__ __forceinline__ static bf16x8 make(floatx4 lo, floatx4 hi) {
-    bf16x8 f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { f[i] = (bf16)lo[i]; f[4 + i] = (bf16)hi[i]; }
-    return f;
-  }
-};
-template <> struct RegFrag<f16, 32> {
-  __device__ __forceinline__ static f16x8 make(floatx4 lo, floatx4 hi) {
-    f16x8 f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { f[i] = (f16)lo[i]; f[4 + i] = (f16)hi[i]; }
-    return f;
-  }
-};
-template <> struct RegFrag<float, 32> {
-  __device__ __forceinline__ static f32frag<8> make(floatx4 lo, floatx4 hi) {
-    f32frag<8> f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { f.v[i] = lo[i]; f.v[4 + i] = hi[i]; }
-    return f;
-  }
-};
-template <> struct RegFrag<float, 16> {
-  __device__ __forceinline__ static f32frag<4> make(floatx4 lo, floatx4 /*unused*/) {
-    f32frag<4> f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f.v[i] = lo[i];
-    return f;
-  }
-};
+// fp32 fragments (general chunk form): a K-block of 16, lane l = 16 g + r
+// holding indices 4g .. 4g+3 of its row, so the 16x16x4 MFMA e contracts
+// over the indices 4g + e.  frag_load reads them from a K-contiguous row
+// (already offset to the lane's row); reg_frag takes them from an fp32
+// accumulator tile, whose lane l holds column l%16 at rows 4(l/16)+i: the
+// accumulator of one product is the B fragment of the next one as it stands.
+typedef f32frag<4> F32Frag;
+__device__ __forceinline__ F32Frag frag_load(const float* row, int kb, int g) {
+  const floatx4 x = *reinterpret_cast<const floatx4*>(row + kb * 16 + 4 * g);
+  return F32Frag{{x[0], x[1], x[2], x[3]}};
+}
+__device__ __forceinline__ F32Frag reg_frag(floatx4 acc) { return F32Frag{{acc[0], acc[1], acc[2], acc[3]}}; }
 
 // Buffer resource (V#) for raw byte-addressed buffer loads and stores: base
 // address, byte range (accesses at offsets >= num_bytes read 0 / are dropped),

@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_prep(
     floatx4 inv_total;
 #pragma unroll
     for (int e = 0; e < 4; ++e) inv_total[e] = 1.0f / total_dec[e];
-    const int kp = pos_of<KBK>(4 * cq);
+    const int kp = 4 * cq;
     // e^-Gamma_t grows with the chunk's decay: an element of K e^-Gamma that
     // is not finite in fp32 (cumulative log decay below about -87 within a
     // chunk) sets the gate-range error bit
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_prep(
       store4(&sm.u.a.kh[t * Sm::LDK + kp], khv);
       store4(&sm.u.a.qt[t * Sm::LDK + kp], qv[jj] * epos);
       const floatx4 kb = kv[jj] * erem;
-      const int tp = pos_of<KBT>(t);
+      const int tp = t;
 #pragma unroll
       for (int e = 0; e < 4; ++e) sm.u.a.kbt[(4 * cq + e) * Sm::LDT + tp] = from_f32<TOp>(kb[e]);
     }
@@ -261,7 +261,6 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_prep(
 
   // ---- phase 2: M and P tiles (lower triangle only) into registers; the
   //      Kt, Qt and Kb^T images go out as fragment blocks.
-  typedef Frag<TOp, KBK> FK;
   constexpr int NTRI = NT * (NT + 1) / 2;
   constexpr int TPW = (2 * NTRI + 3) / 4;  // tiles per wave
   floatx4 tacc[TPW];
@@ -277,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_prep(
       const TOp* brow = sm.u.a.kh + (16 * idx + l16) * Sm::LDK;
 #pragma unroll
       for (int kb = 0; kb < DK / KBK; ++kb)
-        tacc[q2] = mma(tacc[q2], FK::load(arow, kb, g16), FK::load(brow, kb, g16));
+        tacc[q2] = mma(tacc[q2], frag_load(arow, kb, g16), frag_load(brow, kb, g16));
     }
   }
   {
@@ -313,7 +312,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_prep(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * m + 4 * g16 + i;
-        if (isP) sm.u.b.p[r * Sm::LDT + pos_of<KBT>(s)] = from_f32<TOp>(tacc[q2][i]);
+        if (isP) sm.u.b.p[r * Sm::LDT + s] = from_f32<TOp>(tacc[q2][i]);
         else sm.u.b.n[r * Sm::LDF + s] = s < r ? sm.beta[r] * tacc[q2][i] : 0.f;
       }
     }
@@ -382,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_prep(
       if (isP) f.u = *reinterpret_cast<const uint4*>(sm.u.b.p + r * Sm::LDT + kb * KBT + (KBT / 4) * gg);
 #pragma unroll
       for (int e = 0; e < EPF; ++e) {
-        const int s = kb * KBT + idx_in_block<KBT>((KBT / 4) * gg + e);
+        const int s = kb * KBT + (KBT / 4) * gg + e;
         if (isP) {
           if (s > r) f.e[e] = from_f32<TOp>(0.f);
         } else {
@@ -397,7 +396,8 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_prep(
 // w*KB/16 ...), so it loads only its own quarter of each record.
 template <int DK, int C, typename TOp>
 struct ScanGeom {
-  static constexpr int KB = KBOf<TOp>::v;
+  static_assert(sizeof(TOp) == 4, "the general chunk form runs on fp32 operands");
+  static constexpr int KB = kKB32;
   static constexpr int NT = C / 16, NK = DK / 16, NFK = DK / KB, NFT = C / KB;
   static constexpr int KPW = KB / 16;  // key tiles per S K-block
   __host__ __device__ static constexpr int nkb(int mt) { return scan_nkb<KB>(mt); }
@@ -432,9 +432,8 @@ struct ScanLds {
 //   tiles (every wave, so U never has to be exchanged);  O += P U -> LDS;
 //   S = Diag(e^Gamma_n) S + Kb^T U for the wave's key tiles.
 // Accumulator tiles (lane l: column l%16, rows 4(l/16)+i) are B fragments of
-// the next product as they stand (fragment K-positions are permuted per
-// K-block, see pos_in_block), so S, Y and U go to LDS in fragment order and
-// come back with one 16-byte read per lane.  Each wave loads its share of
+// the next product as they stand (reg_frag), so S, Y and U go to LDS in
+// fragment order and come back with one 16-byte read per lane.  Each wave loads its share of
 // every record (its token tile's Kt, Qt, P rows, its key tiles' Kb^T rows,
 // a quarter of T) two chunks ahead, into registers.  Every global access
 // moves 16 bytes per lane: the address unit costs about the same per
@@ -451,15 +450,14 @@ __global__ __launch_bounds__(256) void kda_chunk_scan(
   typedef Rec<DK, C, TOp> R;
   typedef ScanGeom<DK, C, TOp> G;
   typedef ScanRegs<DK, C, TIn, TOp> Regs;
-  constexpr int KB = G::KB, NFK = G::NFK, NFT = G::NFT, KPW = G::KPW, NTB = G::NTB;
+  constexpr int NFK = G::NFK, NFT = G::NFT, KPW = G::KPW, NTB = G::NTB;
   constexpr int BV = 16, NVT = DV / BV;
   // V / o tile: 16-byte pieces, LPR per row, RPI rows per 1 KiB instruction
   constexpr int LPR = BV * (int)sizeof(TIn) / 16, RPI = 64 / LPR, NVQ = C / RPI;
   constexpr int NBD = (C + DK) * 4 / 16;  // lanes holding beta / e^Gamma_n
   static_assert(NVQ >= 1 && NVQ <= 4 && C % RPI == 0 && NBD <= 64, "scan tile shapes");
   static_assert(R::kDec == R::kBeta + C * 4, "beta and e^Gamma_n are contiguous");
-  typedef typename Frag<TOp, KB>::type FT;
-  typedef RegFrag<TOp, KB> RF;
+  typedef F32Frag FT;
   __shared__ ScanLds<DK, C, TIn, TOp> sm;
 
   const int tid = threadIdx.x, lane = tid & 63, g16 = lane >> 4, l16 = lane & 15;
@@ -612,7 +610,7 @@ __global__ __launch_bounds__(256) void kda_chunk_scan(
   auto step = [&](Regs& r, int c, int bp) {
     const int c2 = min(c + 2, nch - 1);
     snapshot(c);
-    if (has_keys) sm.s[kf][lane] = __builtin_bit_cast(uint4, RF::make(S[0], S[KPW - 1]));
+    if (has_keys) sm.s[kf][lane] = __builtin_bit_cast(uint4, reg_frag(S[0]));
     if (has_vq) *reinterpret_cast<uint4*>(&sm.vb[vq_row][vq_part * (16 / sizeof(TIn))]) = r.vv;
     if (w == 0 && lane < NBD) *reinterpret_cast<uint4*>(&sm.bd[bp][4 * lane]) = r.bd;
     __syncthreads();
@@ -630,15 +628,7 @@ __global__ __launch_bounds__(256) void kda_chunk_scan(
       floatx4 Y;
 #pragma unroll
       for (int i = 0; i < 4; ++i) Y[i] = beta[i] * (to_f32(sm.vb[16 * mt + 4 * g16 + i][l16]) - X[i]);
-      // token tile mt is half (mt % KPW) of Y K-block mt / KPW
-      if constexpr (KB == 32) {
-        const auto yf = RF::make(Y, Y);  // low half holds this tile's four values
-        uint2 lo4;
-        __builtin_memcpy(&lo4, &yf, 8);
-        reinterpret_cast<uint2*>(&sm.y[mt / KPW][lane])[mt % KPW] = lo4;
-      } else {
-        sm.y[mt][lane] = __builtin_bit_cast(uint4, RF::make(Y, Y));
-      }
+      sm.y[mt][lane] = __builtin_bit_cast(uint4, reg_frag(Y));   // token tile mt = Y K-block mt
     }
 #pragma unroll
     for (int jj = 0; jj < (NTB + 3) / 4; ++jj)
@@ -659,7 +649,7 @@ __global__ __launch_bounds__(256) void kda_chunk_scan(
     }
     FT uf[NFT];
 #pragma unroll
-    for (int f = 0; f < NFT; ++f) uf[f] = (KB == 32) ? RF::make(U[2 * f], U[(2 * f + 1) % G::NT]) : RF::make(U[f], U[f]);
+    for (int f = 0; f < NFT; ++f) uf[f] = reg_frag(U[f]);
     // O += P U -> output tile in LDS (stored after the next barrier)
     if (has_tile) {
 #pragma unroll

@@ -622,8 +622,15 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan16(
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
             const int64_t el = st_off + 16 * ct * DK + 16 * jj;
-            if (track_f32) store4(track_f32 + ((int64_t)e * H + h) * DV * DK + el, S[ct][jj]);
-            if (to_pool) store4(pool + ((int64_t)se * H + h) * DV * DK + el, S[ct][jj]);
+            // An opaque copy: with a pool of the operand type the cast below
+            // equals the one that built S's LDS fragment at the end of the
+            // previous step, and the compiler would otherwise keep those
+            // converted values live across the loop for this rare store (a
+            // register spill in the 64-column fp16 build).
+            floatx4 sv = S[ct][jj];
+            asm volatile("" : "+v"(sv));
+            if (track_f32) store4(track_f32 + ((int64_t)e * H + h) * DV * DK + el, sv);
+            if (to_pool) store4(pool + ((int64_t)se * H + h) * DV * DK + el, sv);
           }
       }
       next_snap = next_track(c + 1);

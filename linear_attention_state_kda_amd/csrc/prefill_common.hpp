@@ -1,7 +1,7 @@
 // Pieces shared by the two chunked-prefill paths (prefill.hip: the general
-// chunk form, used for fp32 operands; prefill16.hip: the chunk transition
-// form for 16-bit operands): launch constants, the chunk map, fragment
-// helpers and raw buffer loads.
+// chunk form, for fp32 operands; prefill16.hip: the chunk transition form
+// for 16-bit operands): launch constants, the chunk map, record sizes and
+// raw buffer loads.
 #pragma once
 
 #include "kda_common.hpp"
@@ -15,16 +15,18 @@ constexpr int kFB = 1024;   // bytes of one fragment block: 64 lanes x 16 bytes
 constexpr int kNumCU = 256; // MI355X compute units
 constexpr int kSpreadLds = 72 * 1024;  // with the static part, > half of a CU's 160 KiB LDS
 
-// K-block sizes: 32 for the 16-bit 16x16x32 MFMAs; fp32 uses 16 so that one
-// lane's fragment is 16 bytes as well.
-template <typename TOp> struct KBOf { static constexpr int v = (sizeof(TOp) == 4) ? 16 : 32; };
+// K-block size of the general chunk form's fp32 fragments (16x16x4 MFMAs,
+// one 16-byte fragment per lane).
+constexpr int kKB32 = 16;
 
-// Workspace record for one (chunk, head).  A-operand matrices are stored as
-// fragment blocks: block (tile, kb) of an M x K matrix holds, for lane
-// l = 16 g + r, row 16 tile + r at K-block positions kb*KB + (KB/4) g + j.
+// Workspace record of the general chunk form for one (chunk, head), fp32.
+// A-operand matrices are stored as fragment blocks: block (tile, kb) of an
+// M x K matrix holds, for lane l = 16 g + r, row 16 tile + r at K-block
+// positions kb*16 + 4 g + j.
 template <int DK, int C, typename TOp>
 struct Rec {
-  static constexpr int KBK = KBOf<TOp>::v, KBT = KBOf<TOp>::v;
+  static_assert(sizeof(TOp) == 4, "the general chunk form runs on fp32 operands");
+  static constexpr int KBK = kKB32, KBT = kKB32;
   static constexpr int NBK = (C / 16) * (DK / KBK);   // Kt and Qt blocks   (tile = token tile)
   static constexpr int NBB = (DK / 16) * (C / KBT);   // Kb^T blocks        (tile = key tile)
   static constexpr int NBT = (C / 16) * (C / KBT);    // T and P blocks     (tile = token tile)
@@ -45,14 +47,6 @@ __host__ __device__ inline int64_t round_up(int64_t x, int64_t m) { return (x + 
 __host__ __device__ inline int64_t map_bytes(int n_seqs) { return round_up(4 * (int64_t)(n_seqs + 1), 256); }
 __host__ __device__ inline int64_t chunk_upper_bound(int64_t total_tokens, int n_seqs, int C) {
   return total_tokens / C + n_seqs;
-}
-
-// Inverse of pos_in_block: index stored at position p of a K-block.
-template <int KB>
-__device__ __forceinline__ int idx_in_block(int p) {
-  if (KB == 16) return p;
-  const int g = p >> 3, j = p & 7;
-  return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
 }
 
 // A sequence is processed only if its cu_seqlens entries are sane and the
@@ -127,9 +121,6 @@ __host__ __device__ constexpr int scan_tblk(int mt) {
   for (int m = 0; m < mt; ++m) j += scan_nkb<KB>(m);
   return j;
 }
-
-// Scan geometry: four waves per (sequence, head, 16-column tile of S).
-// Wave w owns token tile w (rows of X, Y, O) and S K-block w (key tiles
 
 // 16-bit path (prefill16.hip): record bytes per (chunk, head), and the prep
 // and scan launches once the chunk map is in the workspace.
