@@ -217,7 +217,12 @@ kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, con
  * ckpt_slot[r] and the records of a verify call; write it (one RNE cast) to
  * dst_slot[r] (dst_slot == NULL means in place, dst_slot[r] == ckpt_slot[r]
  * is allowed).  An in-place request with n == 0 touches nothing.  rec_dtype
- * is the dtype of kg_rec.  0 <= accepted_len[r] <= L <= 256. */
+ * is the dtype of kg_rec.  0 <= accepted_len[r] <= L <= 256.  Requests run
+ * concurrently: the destination slots must be distinct from each other and
+ * from every other request's checkpoint slot (a request may write over its
+ * own checkpoint); otherwise the result is a data race.  A request with n
+ * outside [0, L] sets KDA_DEV_ERR_ACCEPT, one with a slot outside
+ * [0, n_slots) KDA_DEV_ERR_SLOT; either is skipped. */
 kda_status kda_commit(kda_pool pool, const int32_t* ckpt_slot, const int32_t* dst_slot,
                       const int32_t* accepted_len, const float* u_rec, const void* kg_rec,
                       int32_t rec_dtype, int32_t n_req, int32_t L, int32_t H, int32_t d_k,
