@@ -711,7 +711,13 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan16(
   } else if (wv == 8 && nch > 0) {   // an empty sequence has no record to touch
     // ---- prefetch wave: lane l touches line l of share vt (one of NVT) of
     //      a record (lanes past the share or the record read nothing), and
-    //      consumes each step's load two steps later
+    //      consumes each step's load two steps later.  With 64-column
+    //      tiles (two per head: half of the record's lines each, four loads
+    //      a step) the touches cost the CU's memory pipeline more than they
+    //      save (four sequences of 8229 tokens 0.76 -> 0.73 ms without them,
+    //      the varlen batch unchanged); there the wave only keeps the
+    //      barrier count.
+    constexpr bool kTouch = NC <= 2;
     constexpr int kLines = (R::kBytes / 128 + NVT - 1) / NVT;
     constexpr int NPL = (kLines + kWave - 1) / kWave;   // loads per step
     int poff[NPL];
@@ -723,7 +729,7 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan16(
     auto touch = [&](uint32_t (&x)[NPL], int c) {
       const auto rs = rec_rsrc(min(c, last));
 #pragma unroll
-      for (int i = 0; i < NPL; ++i) x[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, poff[i], 0, 0);
+      for (int i = 0; i < NPL; ++i) x[i] = kTouch ? __builtin_amdgcn_raw_buffer_load_b32(rs, poff[i], 0, 0) : 0u;
     };
     uint32_t pa[NPL], pb[NPL];
     touch(pa, kScanPrefetch - 2);
