@@ -319,14 +319,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   // after the prefill 147 -> 134 us).  Non-temporal 8-byte halves, each
   // line completed by a second wave, made the prefill slower instead.
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  // Gate range: a 16-bit element whose exponent field is all ones rounded
+  // to infinity (or is NaN).  Adding the field's lowest bit to the masked
+  // field carries into the sign position exactly then, for both halves of a
+  // word at once.
+  constexpr uint32_t kExpMask = std::is_same<T, f16>::value ? 0x7C007C00u : 0x7F807F80u;
+  constexpr uint32_t kExpLow = std::is_same<T, f16>::value ? 0x04000400u : 0x00800080u;
+  uint32_t kh_bad = 0;
 #pragma unroll
   for (int kb = 0; kb < NFK; ++kb) {
     __builtin_nontemporal_store(__builtin_bit_cast(u32x4, ktf[kb]),
                                 reinterpret_cast<u32x4*>(rec + R::kKt + (w * NFK + kb) * kFB + lane * 16));
     __builtin_nontemporal_store(__builtin_bit_cast(u32x4, qtf[kb]),
                                 reinterpret_cast<u32x4*>(rec + R::kQt + (w * NFK + kb) * kFB + lane * 16));
-    sm.r1.kh[w][kb][lane] = __builtin_bit_cast(uint4, khf[kb]);
+    const uint4 kh = __builtin_bit_cast(uint4, khf[kb]);
+    for (uint32_t wd : {kh.x, kh.y, kh.z, kh.w}) kh_bad |= (wd & kExpMask) + kExpLow;
+    sm.r1.kh[w][kb][lane] = kh;
   }
+  if (__builtin_amdgcn_ballot_w64((kh_bad & 0x80008000u) != 0) != 0 && lane == 0) set_err(dev_err, 1u << 5);
 
   // 0/1 selection fragments: sel[hf] picks channel 16 hf + r of a K-block, so
   // the product X sel[hf] is the transpose of X's 16 x 16 tile hf, in the
@@ -353,11 +363,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   //      then holds P[16w + r][16jt + 4g + e], the row form of P_w,jt.
   floatx4 ptile[4], nrow[4];
   const int rr = 16 * w + r;  // this lane's row of P, M, N, T
-  // Wave 3 reads every Kh tile: an element whose exponent field is all ones
-  // rounded to infinity (or is NaN), so the chunk is beyond the supported
-  // gate range
-  constexpr uint32_t kExp = std::is_same<T, f16>::value ? 0x7C00u : 0x7F80u, kExp2 = kExp << 16;
-  uint32_t kh_bad = 0;
 #pragma unroll
   for (int jt = 0; jt < 4; ++jt) {
     ptile[jt] = nrow[jt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -365,12 +370,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     floatx4 pm = {0.f, 0.f, 0.f, 0.f}, pp = pm;
 #pragma unroll
     for (int kb = 0; kb < NFK; ++kb) {
-      const uint4 araw = sm.r1.kh[jt][kb][lane];
-      const F8 a = __builtin_bit_cast(F8, araw);
+      const F8 a = __builtin_bit_cast(F8, sm.r1.kh[jt][kb][lane]);
       pm = mma(pm, a, ktf[kb]);
       pp = mma(pp, a, qtf[kb]);
-      if (w == 3)
-        for (uint32_t wd : {araw.x, araw.y, araw.z, araw.w}) kh_bad |= ((wd & kExp) == kExp) | ((wd & kExp2) == kExp2);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -379,7 +381,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
       nrow[jt][e] = s < rr ? beta * pm[e] : 0.f;
     }
   }
-  if (w == 3 && __builtin_amdgcn_ballot_w64(kh_bad != 0) != 0 && lane == 0) set_err(dev_err, 1u << 5);
   // P fragments: block (w, b) = [P_w,2b | P_w,2b+1] for token blocks b up to the diagonal
 #pragma unroll
   for (int b = 0; b < 2; ++b)
