@@ -13,9 +13,10 @@
 // and cast once into the pool dtype (SGLang PR #34820 summary,
 // implementation breakdown item 2 and the kda_prefill.py excerpt).
 //
-// Three launches on the caller's stream:
+// Three launches on the caller's stream (two for a single sequence):
 //  1. kda_chunk_map: one block turns cu_seqlens into per-sequence chunk offsets
-//     (and validates them) without any host synchronisation.
+//     (and validates them) without any host synchronisation.  A single
+//     sequence's chunks start at slot 0 and need no map.
 //  2. kda_chunk_prep: one workgroup per (chunk, head), fully parallel.  Computes
 //     everything that does not depend on the state -- Kt, Qt, Kb^T, T, P, beta,
 //     e^Gamma_n -- and writes it as one record to the workspace, with every
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_prep(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
   const int h = blockIdx.x % H;
   const int j = blockIdx.x / H;  // global chunk slot
-  if (j >= off[n_seqs]) return;
+  if (off != nullptr && j >= off[n_seqs]) return;
   // sequence owning chunk slot j: largest seq with off[seq] <= j
   int lo = 0, hi = n_seqs - 1;
   while (lo < hi) {
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_prep(
   const int seq = lo;
   int t_beg, len, nch;
   if (!seq_ok(cu, off, seq, total, C, t_beg, len, nch)) return;
-  const int c = j - off[seq];
+  const int c = j - chunk_base(off, seq);
   if (c >= nch) return;
   const int t0 = t_beg + c * C;
   const int n = min(C, len - c * C);
@@ -471,7 +472,11 @@ __global__ __launch_bounds__(256) void kda_chunk_scan(
   if (pair >= n_seqs * H) return;
   const int seq = pair / H, h = pair % H;
   int t_beg, len, nch;
-  if (!seq_ok(cu, off, seq, total, C, t_beg, len, nch)) return;
+  if (!seq_ok(cu, off, seq, total, C, t_beg, len, nch)) {
+    // with no chunk map (one sequence) nothing else has checked cu_seqlens
+    if (off == nullptr && blockIdx.x == 0 && tid == 0) set_err(dev_err, 1u << 3);
+    return;
+  }
   const int v0 = vt * BV;
   const bool lead = (vt == 0 && h == 0);
 
@@ -546,7 +551,7 @@ __global__ __launch_bounds__(256) void kda_chunk_scan(
   // V / o piece of this lane in wave w's 1 KiB instruction: row, 16-byte part
   const int vq_row = RPI * w + lane / LPR, vq_part = lane % LPR;
   const int vq_off = (int)((int64_t)vq_row * vrow * (int)sizeof(TIn)) + 16 * vq_part;
-  const uint8_t* rec_seq = recs + ((int64_t)h * cap + off[seq]) * R::kBytes;
+  const uint8_t* rec_seq = recs + ((int64_t)h * cap + chunk_base(off, seq)) * R::kBytes;
 
   // Per-chunk buffer resources: the record, and the chunk's rows of V / o
   // (reads past the last row return 0 and stores there are dropped; those
@@ -715,14 +720,18 @@ struct WsView {
   uint8_t* recs;   // records, [head][chunk slot]
 };
 
+// A single sequence needs no chunk map: the kernels take its chunk slots
+// from cu_seqlens alone (and its scan flags a malformed pair), which saves
+// a dependent launch.
 WsView map_chunks(const PrefillArgs& a, hipStream_t st, int C) {
   WsView w;
   w.cap = chunk_upper_bound(a.total_tokens, a.n_seqs, C);
   uint8_t* ws = static_cast<uint8_t*>(a.workspace);
-  w.off = reinterpret_cast<int32_t*>(ws);
+  w.off = a.n_seqs > 1 ? reinterpret_cast<int32_t*>(ws) : nullptr;
   w.recs = ws + map_bytes(a.n_seqs);
-  hipLaunchKernelGGL(kda_chunk_map, dim3(1), dim3(kThreads), 0, st, a.cu_seqlens, a.n_seqs,
-                     a.total_tokens, C, w.cap, w.off, a.dev_err);
+  if (w.off != nullptr)
+    hipLaunchKernelGGL(kda_chunk_map, dim3(1), dim3(kThreads), 0, st, a.cu_seqlens, a.n_seqs,
+                       a.total_tokens, C, w.cap, w.off, a.dev_err);
   return w;
 }
 

@@ -13,7 +13,7 @@
 // two dependent products (Kt S, then Z Y) instead of four, and a record
 // holds Kt, Qt, Z, Pw and e^Gamma_n (54.5 KiB at d_k = 128, C = 64).
 //
-// Two launches after the chunk map (prefill.hip):
+// Two launches after the chunk map (prefill.hip; none for a single sequence):
 //  * kda_chunk_prep16: one workgroup per (chunk, head), fully parallel;
 //    writes the record as MFMA A-operand fragment blocks.
 //  * kda_chunk_scan16: one workgroup per (sequence, head, column tile of S:
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   // be in the memory-side cache.
   const int h = blockIdx.x % H;
   const int j = (int)(cap - 1) - (int)(blockIdx.x / H);  // global chunk slot
-  if (j >= off[n_seqs]) return;
+  if (off != nullptr && j >= off[n_seqs]) return;
   int lo = 0, hi = n_seqs - 1;   // sequence owning chunk slot j
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   }
   int t_beg, len, nch;
   if (!seq_ok(cu, off, lo, total, C, t_beg, len, nch)) return;
-  const int c = j - off[lo];
+  const int c = j - chunk_base(off, lo);
   if (c >= nch) return;
   const int t0 = t_beg + c * C;
   const int n = min(C, len - c * C);
@@ -545,7 +545,11 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan16(
   if (pair >= n_seqs * H) return;
   const int seq = pair / H, h = pair % H;
   int t_beg, len, nch;
-  if (!seq_ok(cu, off, seq, total, C, t_beg, len, nch)) return;
+  if (!seq_ok(cu, off, seq, total, C, t_beg, len, nch)) {
+    // with no chunk map (one sequence) nothing else has checked cu_seqlens
+    if (off == nullptr && blockIdx.x == 0 && tid == 0) set_err(dev_err, 1u << 3);
+    return;
+  }
   const int v0 = vt * BV;
   const bool lead = (vt == 0 && h == 0);
 
@@ -569,7 +573,7 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan16(
 
   const int64_t vrow = (int64_t)H * DV;
   const int lane_off = lane * 16;
-  const uint8_t* rec_seq = recs + ((int64_t)h * cap + off[seq]) * R::kBytes;
+  const uint8_t* rec_seq = recs + ((int64_t)h * cap + chunk_base(off, seq)) * R::kBytes;
   auto rec_rsrc = [&](int c) { return buffer_rsrc(rec_seq + (int64_t)c * R::kBytes, R::kBytes); };
   // Rows of chunk c of V / o in this tile (reads past the last row return 0,
   // stores there are dropped).

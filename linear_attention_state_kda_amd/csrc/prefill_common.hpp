@@ -49,15 +49,21 @@ __host__ __device__ inline int64_t chunk_upper_bound(int64_t total_tokens, int n
   return total_tokens / C + n_seqs;
 }
 
+// Chunk map: sequence i owns chunk slots off[i] .. off[i + 1] - 1.  A
+// single sequence needs no map (off == nullptr): its chunks take slots
+// 0 .. ceil(len / C) - 1, and ceil(len / C) <= total / C + 1 slots exist.
+__device__ __forceinline__ int chunk_base(const int32_t* off, int seq) { return off ? off[seq] : 0; }
+
 // A sequence is processed only if its cu_seqlens entries are sane and the
-// chunk map gave it exactly ceil(len / C) chunks.
+// chunk map (if any) gave it exactly ceil(len / C) chunks.
 __device__ __forceinline__ bool seq_ok(const int32_t* cu, const int32_t* off, int seq,
                                        int64_t total, int C, int& t_beg, int& len, int& nch) {
   t_beg = cu[seq];
   const int t_end = cu[seq + 1];
   len = t_end - t_beg;
   nch = (len + C - 1) / C;
-  return t_beg >= 0 && len >= 0 && (int64_t)t_end <= total && off[seq + 1] - off[seq] == nch;
+  return t_beg >= 0 && len >= 0 && (int64_t)t_end <= total &&
+         (off == nullptr || off[seq + 1] - off[seq] == nch);
 }
 
 // 16 bytes viewed as a fragment of TOp elements.

@@ -255,6 +255,14 @@ def test_device_errors_are_flagged():
     bad_cu = np.array([0, 100, 90], dtype=np.int32)
     g2 = run_gpu(case2, toks2, bad_cu)
     assert g2["err"] & kda.DEV_ERR_SEQLEN
+    # a single sequence has no chunk map: its scan flags the pair itself and
+    # writes nothing (beyond the 64 tokens, negative start, decreasing)
+    case3 = wl.prefill_case([64], 2, 128, 128, 64, "bf16", "f32", 4, [-1], [0], [], False, seed=16)
+    toks3, _ = tokens(case3)
+    for bad in ([0, 100], [-1, 10], [40, 20]):
+        g3 = run_gpu(case3, toks3, np.array(bad, dtype=np.int32))
+        assert g3["err"] & kda.DEV_ERR_SEQLEN, bad
+        assert untouched(g3["pool"], [0, 1, 2, 3], "f32"), bad
 
 
 # ---------------------------------------------------------------- full-size workloads
