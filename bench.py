@@ -46,6 +46,9 @@ import linear_attention_state_kda_amd as kda  # noqa: E402
 import workloads as wl  # noqa: E402
 
 HBM_PEAK = 8.0e12            # bytes/s, MI355X HBM3E
+# the launches of one prefill call: a single sequence needs no chunk map
+PREFILL_KERNELS = {False: "kda_chunk_prefill (kda_chunk_prep16 + kda_chunk_scan16)",
+                   True: "kda_chunk_prefill (kda_chunk_map + kda_chunk_prep16 + kda_chunk_scan16)"}
 CSRC = os.path.join(ROOT, "linear_attention_state_kda_amd", "csrc")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "prefill_traffic.md")
 BF16_PEAK = 2.5e15           # FLOP/s, dense bf16 MFMA
@@ -185,7 +188,7 @@ def time_leg(dev, st, case, label, reps=5):
             "ms_median": ms, "tokens_per_s": T / s_,
             "hbm_GBps": bytes_ / s_ / 1e9, "hbm_frac": bytes_ / s_ / HBM_PEAK,
             "mfma_TFLOPs": flops / s_ / 1e12, "mfma_frac": flops / s_ / BF16_PEAK,
-            "roofline": {"kernel": "kda_chunk_prefill (kda_chunk_map + kda_chunk_prep16 + kda_chunk_scan16)",
+            "roofline": {"kernel": PREFILL_KERNELS[n > 1],
                          "bound": "hbm", "achieved": bytes_ / s_ / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                          "frac": bytes_ / s_ / HBM_PEAK, "algorithmic_bytes_per_launch": bytes_,
                          "algorithmic_flop_per_launch": flops, "mfma_frac": flops / s_ / BF16_PEAK,
@@ -455,7 +458,7 @@ def main():
     if dominant == "prefill":
         achieved = p_bytes / p_s / 1e9
         traffic, traffic_src = measured_prefill_traffic()
-        roof = {"kernel": "kda_chunk_prefill (kda_chunk_map + kda_chunk_prep16 + kda_chunk_scan16)",
+        roof = {"kernel": PREFILL_KERNELS[False],
                 "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                 "frac": achieved * 1e9 / HBM_PEAK, "traffic": traffic, "traffic_source": traffic_src,
                 "algorithmic_bytes_per_launch": p_bytes, "algorithmic_flop_per_launch": p_flops,
