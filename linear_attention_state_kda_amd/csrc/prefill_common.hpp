@@ -129,8 +129,7 @@ __host__ __device__ constexpr int scan_tblk(int mt) {
 }
 
 // 16-bit path (prefill16.hip): record bytes per (chunk, head), and the prep
-// and scan launches once the chunk map (off; nullptr for one sequence) is
-// in the workspace.
+// and scan launches once the chunk map is in the workspace.
 int64_t rec16_bytes();
 hipError_t launch_prefill16(const PrefillArgs& a, hipStream_t st, int64_t cap, const int32_t* off,
                             uint8_t* recs);
