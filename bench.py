@@ -249,6 +249,19 @@ def measured_prefill_traffic():
         f"here); not measured in this run"
 
 
+def committed_copy_traffic_ratio():
+    """HBM bytes over algorithmic bytes of the fork copy, from the committed
+    FETCH_SIZE / WRITE_SIZE profile (the copy's sources are read once per
+    child, the repeats hitting the memory-side cache), or None if absent."""
+    try:
+        for line in open(os.path.join(ROOT, "profiles", "state_paths_traffic.md")):
+            if line.startswith("| copy"):
+                return float(line.strip().strip("|").split("|")[-1])
+    except (OSError, ValueError):
+        pass
+    return None
+
+
 def cpu_model():
     """The host CPU's model name (from /proc/cpuinfo when readable)."""
     try:
@@ -455,6 +468,7 @@ def main():
     state_calls = ("verify", "commit", "commit_align", "conv_compact", "copy", "conv_fork")
     gbs = {c: sp["bytes"][c] / (sel[c] * 1e-3) / 1e9 for c in state_calls}
     dominant = max(calls, key=lambda c: sel[c])
+    copy_ratio = committed_copy_traffic_ratio()
     if dominant == "prefill":
         achieved = p_bytes / p_s / 1e9
         traffic, traffic_src = measured_prefill_traffic()
@@ -489,6 +503,13 @@ def main():
                "hbm_frac": gbs[c] * 1e9 / HBM_PEAK,
                "hbm_frac_warm": sp["bytes"][c] / (ms[c] * 1e-3) / HBM_PEAK} for c in state_calls},
         "roofline": roof,
+        "copy_hbm_traffic": None if copy_ratio is None else {
+            "GBps": gbs["copy"] * copy_ratio, "hbm_frac": gbs["copy"] * copy_ratio * 1e9 / HBM_PEAK,
+            "ratio": copy_ratio,
+            "note": "the copy's algorithmic bytes charge every pair a full source read; its 64 sources are "
+                    "read once per child and the repeats hit the memory-side cache, so its HBM traffic is "
+                    "this ratio of the algorithmic bytes (profiles/state_paths_traffic.md, rocprofv3 "
+                    "FETCH_SIZE + WRITE_SIZE; not measured in this run)"},
         "hbm_reference": hbm_reference,
         "cold": None if cold is None else {
             "note": "L2 and MALL flushed by a 512 MiB write and the checkpoints restored before each step",

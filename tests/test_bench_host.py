@@ -60,3 +60,13 @@ def test_head_subset_draw_matches_full_draw():
     part = wl.token_inputs(50, 6, 16, 16, "bf16", 3, heads=[4, 1])
     for n in "qkvgb":
         assert torch.equal(part[n], full[n][:, [4, 1]])
+
+
+def test_copy_traffic_ratio_is_read_from_the_committed_profile():
+    """The fork copy's HBM-traffic ratio comes from the committed counter
+    summary: its 64 sources are read once per child, so the ratio lies
+    between the one-read-per-source floor (0.625 of the algorithmic bytes:
+    64 of 256 source reads plus all 256 writes) and 1."""
+    import bench
+    r = bench.committed_copy_traffic_ratio()
+    assert r is not None and 0.62 <= r <= 1.0

@@ -232,6 +232,18 @@ def test_final_over_own_init_slot():
     check_case(case, toks, cu, g, [0, 1])
 
 
+def test_single_sequence_inside_the_buffer():
+    """One sequence that starts past the buffer's first token and ends before
+    its last (cu_seqlens = [100, 330] over 400 tokens: three full chunks and
+    a 38-token tail): a single sequence gets no chunk map, so its records
+    take chunk slots from 0 while its tokens start at row 100."""
+    case = wl.prefill_case([400], 4, 128, 128, 64, "bf16", "f32", 4, [1], [2], [(0, 2, 3)], True, seed=17)
+    toks, _ = tokens(case)
+    cu = np.array([100, 330], dtype=np.int32)
+    g = run_gpu(case, toks, cu)
+    check_case(case, toks, cu, g, list(range(4)))
+
+
 def test_bitwise_deterministic():
     case = wl.prefill_case([500, 70], 4, 128, 128, 64, "bf16", "f32", 4, [-1, -1], [0, 1],
                            [(0, 5, 2)], True, seed=13)
