@@ -244,6 +244,20 @@ def test_single_sequence_inside_the_buffer():
     check_case(case, toks, cu, g, list(range(4)))
 
 
+@pytest.mark.parametrize("length", [0, 1, 64, 65])
+def test_single_sequence_edge_lengths(length):
+    """One sequence, so no chunk map: empty (a zero-token buffer: the final
+    state and the chunk-0 snapshot are the initial state cast once), one
+    token, exactly one chunk (its end snapshot is the final state), one
+    chunk and one token."""
+    tracks = [(0, 0, 2)] + ([(0, length // 64, 3)] if length >= 64 else [])
+    case = wl.prefill_case([length], 2, 128, 128, 64, "bf16", "f32", 6, [4], [1], tracks, True,
+                           seed=18 + length)
+    toks, cu = tokens(case)
+    g = run_gpu(case, toks, cu)
+    check_case(case, toks, cu, g, [0, 1])
+
+
 def test_bitwise_deterministic():
     case = wl.prefill_case([500, 70], 4, 128, 128, 64, "bf16", "f32", 4, [-1, -1], [0, 1],
                            [(0, 5, 2)], True, seed=13)
