@@ -136,6 +136,9 @@ kda_status kda_chunk_prefill_workspace(int32_t n_seqs, int64_t total_tokens, int
  *
  * q, k, v, g, b   inputs in `in_dtype` (layouts above); o output, same dtype.
  * cu_seqlens      int32 [n_seqs + 1] token offsets, non-decreasing, last <= total_tokens.
+ * sizes           total_tokens <= INT32_MAX, (total_tokens / chunk + n_seqs) * H
+ *                 <= UINT32_MAX and n_seqs * H * 8 <= INT32_MAX (the launch
+ *                 grids' index range), else KDA_ERR_UNSUPPORTED.
  * pool            state pool; pool.H, d_k, d_v must equal H, d_k, d_v.
  * init_slot       int32 [n_seqs]: slot holding the initial state of sequence
  *                 i (upcast exactly to fp32), or -1 for a zero state.

@@ -56,6 +56,8 @@ kda_status kda_chunk_prefill_workspace(int32_t n_seqs, int64_t total_tokens, int
   if (!dtype_ok(in_dtype)) return KDA_ERR_UNSUPPORTED;
   if (!kda::prefill_supported(d_k, d_v, chunk, in_dtype, KDA_F32)) return KDA_ERR_UNSUPPORTED;
   if (total_tokens > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  if ((total_tokens / chunk + n_seqs) * (int64_t)H > UINT32_MAX || (int64_t)n_seqs * H * 8 > INT32_MAX)
+    return KDA_ERR_UNSUPPORTED;
   *bytes = kda::prefill_workspace_bytes(n_seqs, total_tokens, H, d_k, d_v, chunk, in_dtype);
   return KDA_OK;
 }
@@ -78,6 +80,10 @@ kda_status prefill_check(const void* q, const void* k, const void* v, const void
   if (!dtype_ok(in_dtype)) return KDA_ERR_UNSUPPORTED;
   if (!kda::prefill_supported(d_k, d_v, chunk, in_dtype, pool.dtype)) return KDA_ERR_UNSUPPORTED;
   if (total_tokens > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  // launch grids: one workgroup per (chunk slot, head) for the prep, up to
+  // eight per (sequence, head) for the scan
+  if ((total_tokens / chunk + n_seqs) * (int64_t)H > UINT32_MAX || (int64_t)n_seqs * H * 8 > INT32_MAX)
+    return KDA_ERR_UNSUPPORTED;
   kda_status ps = check_pool(pool, H, d_k, d_v);
   if (ps != KDA_OK) return ps;
   if (n_seqs == 0) return KDA_OK;

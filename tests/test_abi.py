@@ -85,6 +85,9 @@ def test_prefill_host_errors(L):
     for name in ("q", "k", "v", "g", "o", "tf32"):   # every vector-accessed buffer must be 16-byte aligned
         assert prefill(L, **{name: ctypes.c_void_p(0x1008)}) == 1, name
     assert prefill(L, T=1 << 33) == 2
+    # launch grids beyond their index range: (chunk slots x heads) and (sequences x heads x 8)
+    assert prefill(L, T=(1 << 31) - 1, H=129, pool=pool(H=129)) == 2
+    assert prefill(L, n_seqs=1 << 20, H=256, pool=pool(H=256)) == 2
     assert prefill(L, flags=2) == 1             # unknown flag bit
     # nothing to do: returns before touching anything
     assert prefill(L, n_seqs=0, q=None, cu=None) == 0
@@ -98,6 +101,8 @@ def test_workspace_query(L):
     assert kda.prefill_workspace_bytes(1, 64, 2, 16, 16, 16, __import__("torch").float32) > 0
     assert L.kda_chunk_prefill_workspace(1, 64, 2, 32, 32, 16, 2, ctypes.byref(out)) == 2
     assert L.kda_chunk_prefill_workspace(1, 64, 2, 128, 128, 64, 2, None) == 1
+    assert L.kda_chunk_prefill_workspace(1, (1 << 31) - 1, 129, 128, 128, 64, 2, ctypes.byref(out)) == 2
+    assert L.kda_chunk_prefill_workspace(1 << 20, 64, 256, 128, 128, 64, 2, ctypes.byref(out)) == 2
 
 
 def test_verify_commit_copy_host_errors(L):
