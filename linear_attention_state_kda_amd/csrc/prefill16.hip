@@ -13,7 +13,7 @@
 // two dependent products (Kt S, then Z Y) instead of four, and a record
 // holds Kt, Qt, Z, Pw and e^Gamma_n (54.5 KiB at d_k = 128, C = 64).
 //
-// Two launches after the chunk map (prefill.hip; none for a single sequence):
+// Two launches after the chunk map (prefill.hip; a single sequence needs no map):
 //  * kda_chunk_prep16: one workgroup per (chunk, head), fully parallel;
 //    writes the record as MFMA A-operand fragment blocks.
 //  * kda_chunk_scan16: one workgroup per (sequence, head, column tile of S:
