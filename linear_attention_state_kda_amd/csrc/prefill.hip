@@ -15,8 +15,9 @@
 //
 // Three launches on the caller's stream (two for a single sequence):
 //  1. kda_chunk_map: one block turns cu_seqlens into per-sequence chunk offsets
-//     (and validates them) without any host synchronisation.  A single
-//     sequence's chunks start at slot 0 and need no map.
+//     (and validates them) and the scan's order of the sequences (longest
+//     first), without any host synchronisation.  A single sequence's chunks
+//     start at slot 0 and need no map.
 //  2. kda_chunk_prep: one workgroup per (chunk, head), fully parallel.  Computes
 //     everything that does not depend on the state -- Kt, Qt, Kb^T, T, P, beta,
 //     e^Gamma_n -- and writes it as one record to the workspace, with every
@@ -49,6 +50,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_map(const int32_t* __restr
                                                           int32_t* __restrict__ off,
                                                           int32_t* __restrict__ dev_err) {
   __shared__ int32_t s_scan[kThreads];
+  __shared__ int32_t s_nch[kOrderMax];
   __shared__ int64_t s_carry;
   if (threadIdx.x == 0) { s_carry = 0; off[0] = 0; }
   __syncthreads();
@@ -60,6 +62,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_map(const int32_t* __restr
       const int a = cu[i], b2 = cu[i + 1];
       bad = a < 0 || b2 < a || (int64_t)b2 > total;
       nch = bad ? 0 : (b2 - a + C - 1) / C;
+      if (n_seqs <= kOrderMax) s_nch[i] = nch;
     }
     s_scan[threadIdx.x] = nch;
     __syncthreads();
@@ -81,6 +84,20 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_map(const int32_t* __restr
     __syncthreads();
     if (threadIdx.x == kThreads - 1) s_carry += s_scan[kThreads - 1];
     __syncthreads();
+  }
+  // The scan's order: most chunks first (ties by index), so the longest
+  // serial chains start first and the workgroups that start last are
+  // short ones (list scheduling, longest first); batch order past
+  // kOrderMax sequences, where ranking them here would cost more.
+  int32_t* const ord = off + n_seqs + 1;
+  for (int i = threadIdx.x; i < n_seqs; i += kThreads) {
+    int place = i;
+    if (n_seqs <= kOrderMax) {
+      const int ni = s_nch[i];
+      place = 0;
+      for (int j = 0; j < n_seqs; ++j) place += (s_nch[j] > ni || (s_nch[j] == ni && j < i)) ? 1 : 0;
+    }
+    ord[place] = i;
   }
 }
 
@@ -470,7 +487,7 @@ __global__ __launch_bounds__(256) void kda_chunk_scan(
   const int vt = slot_ % NVT;
   const int pair = (slot_ / NVT) * kXcd + xcd;
   if (pair >= n_seqs * H) return;
-  const int seq = pair / H, h = pair % H;
+  const int seq = seq_at(off, n_seqs, pair / H), h = pair % H;
   int t_beg, len, nch;
   if (!seq_ok(cu, off, seq, total, C, t_beg, len, nch)) {
     // with no chunk map (one sequence) nothing else has checked cu_seqlens

@@ -543,7 +543,7 @@ __global__ __launch_bounds__(kScanThreads) void kda_chunk_scan16(
   const int vt = slot_ % NVT;
   const int pair = (slot_ / NVT) * kXcd + xcd;
   if (pair >= n_seqs * H) return;
-  const int seq = pair / H, h = pair % H;
+  const int seq = seq_at(off, n_seqs, pair / H), h = pair % H;
   int t_beg, len, nch;
   if (!seq_ok(cu, off, seq, total, C, t_beg, len, nch)) {
     // with no chunk map (one sequence) nothing else has checked cu_seqlens

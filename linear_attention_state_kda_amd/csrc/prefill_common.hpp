@@ -44,7 +44,12 @@ struct Rec {
 };
 
 __host__ __device__ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
-__host__ __device__ inline int64_t map_bytes(int n_seqs) { return round_up(4 * (int64_t)(n_seqs + 1), 256); }
+// The chunk map in the workspace: off[n_seqs + 1], then the scan's order of
+// the sequences, ord[n_seqs].
+__host__ __device__ inline int64_t map_bytes(int n_seqs) { return round_up(4 * (2 * (int64_t)n_seqs + 1), 256); }
+// Batches up to this many sequences are scanned longest first (the map
+// ranks them); larger ones in batch order.
+constexpr int kOrderMax = 128;
 __host__ __device__ inline int64_t chunk_upper_bound(int64_t total_tokens, int n_seqs, int C) {
   return total_tokens / C + n_seqs;
 }
@@ -53,6 +58,11 @@ __host__ __device__ inline int64_t chunk_upper_bound(int64_t total_tokens, int n
 // single sequence needs no map (off == nullptr): its chunks take slots
 // 0 .. ceil(len / C) - 1, and ceil(len / C) <= total / C + 1 slots exist.
 __device__ __forceinline__ int chunk_base(const int32_t* off, int seq) { return off ? off[seq] : 0; }
+// The sequence at place i of the scan's order (ord, written by the chunk
+// map after off); without a map, i itself.
+__device__ __forceinline__ int seq_at(const int32_t* off, int n_seqs, int i) {
+  return off ? off[n_seqs + 1 + i] : i;
+}
 
 // A sequence is processed only if its cu_seqlens entries are sane and the
 // chunk map (if any) gave it exactly ceil(len / C) chunks.
