@@ -475,6 +475,9 @@ def main():
         roof = {"kernel": PREFILL_KERNELS[False],
                 "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                 "frac": achieved * 1e9 / HBM_PEAK, "traffic": traffic, "traffic_source": traffic_src,
+                # the same call's measured HBM bytes over its time: how busy HBM actually is
+                "traffic_GBps": None if traffic is None else traffic / p_s / 1e9,
+                "traffic_frac": None if traffic is None else traffic / p_s / HBM_PEAK,
                 "algorithmic_bytes_per_launch": p_bytes, "algorithmic_flop_per_launch": p_flops,
                 "mfma_frac": p_flops / p_s / BF16_PEAK, "avg_launch_ms": sel["prefill"],
                 "timing": basis}
