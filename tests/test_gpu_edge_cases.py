@@ -6,6 +6,8 @@ fp64 oracle.
   passes of its prefix and the scan sees 1,400 (sequence, head) pairs
   (64-column tiles); initial states from pool slots and zeros, a snapshot
   per sequence that has a full chunk.
+* Batches of 128 and 129 sequences: the two sides of the chunk map's
+  longest-first ranking limit.
 * Degenerate gates, the special cases the recurrence reduces to:
   g = 0 with b = -30 (beta = sigmoid(-30) ~ 9e-14): no decay and no write,
   so the state stays the initial state and o_t = S0^T q_t;
@@ -35,6 +37,24 @@ def test_many_short_sequences():
     tracks = [(i, 1, 1400 + i) for i in range(n) if lens[i] >= 64] + [(3, 0, -1)]
     case = wl.prefill_case(lens, 2, 128, 128, 64, "bf16", "f32", 1400 + n, init, final, tracks, True, seed=95,
                            name="700 short sequences H=2")
+    toks, cu = wl.prefill_tokens(case)
+    g = run_gpu(case, toks, cu)
+    check_case(case, toks, cu, g, [0, 1])
+
+
+@pytest.mark.parametrize("n", [128, 129])
+def test_batch_at_the_ordering_limit(n):
+    """Up to 128 sequences the chunk map ranks them longest first for the
+    scan (ties by index); 129 take the batch order.  Lengths 0..300 with many
+    equal chunk counts, H = 2 (64-column scan tiles): every sequence against
+    the oracle in both regimes."""
+    lens = np.random.default_rng([97, n]).integers(0, 301, n)
+    lens[[0, 7, n - 1]] = [0, 300, 64]
+    init = [(n + i) if i % 4 == 0 else -1 for i in range(n)]
+    final = list(range(n))
+    tracks = [(i, 1, 2 * n + i) for i in range(n) if lens[i] >= 64]
+    case = wl.prefill_case(lens, 2, 128, 128, 64, "bf16", "f32", 3 * n, init, final, tracks, True, seed=97,
+                           name=f"{n} sequences H=2")
     toks, cu = wl.prefill_tokens(case)
     g = run_gpu(case, toks, cu)
     check_case(case, toks, cu, g, [0, 1])
