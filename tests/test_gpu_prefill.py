@@ -303,6 +303,19 @@ def test_single_layer_full():
     print("single-layer worst rel", w)
 
 
+def test_single_layer_fp16_sampled_heads():
+    """The single-layer shape (T = 8229: 128 chunks and a 37-token tail,
+    H = 32) with fp16 inputs and an fp16 pool from a pool initial state:
+    heads 0, 13 and 31 against the oracle over the whole sequence, and the
+    snapshot at c = 128 rounded once into the pool."""
+    case = wl.prefill_case([8229], 32, 128, 128, 64, "f16", "f16", 4, [2], [0], [(0, 128, 1)], True, seed=19,
+                           name="single-layer fp16")
+    toks, cu = tokens(case)
+    g = run_gpu(case, toks, cu)
+    w = check_case(case, toks, cu, g, [0, 13, 31])
+    print("single-layer fp16 worst", w)
+
+
 @pytest.mark.parametrize("pool_dtype", ["f32", "f16", "bf16"])
 def test_varlen_sampled_heads(pool_dtype):
     """16 sequences (lengths 512..16384), H = 32, per-sequence snapshots,
