@@ -7,6 +7,8 @@
 * Split invariance: prefilling T1 = 4 full chunks, then the rest of the
   sequence from the final state left in an fp32 pool slot, reproduces the
   one-shot run bit for bit (the same chunks meet the same fp32 state).
+* Concurrent calls on three streams (two prefills with their own
+  workspaces and a verify) equal the same calls one after the other.
 * Graph capture: prefill, verify, commit, align commit (with its next-step
   outputs), copy and the conv-state update captured once in a HIP graph and
   replayed three times, with eager work and synchronisations in between,
@@ -75,6 +77,53 @@ def test_prefill_split_invariance():
     assert torch.equal(pool[2], pool[1])                 # state after 4 chunks = snapshot c = 4
     assert torch.equal(torch.cat([o_a, o_b]), o_one)
     assert torch.equal(pool[3], pool[0])                 # final states
+
+
+def test_concurrent_calls_on_streams():
+    """Two prefills (each with its own workspace) and a verify issued on
+    three streams at once give, bit for bit, what they give one after the
+    other: the library keeps no state between calls beyond the caller's
+    buffers."""
+    def setup(seed, lens):
+        toks = wl.token_inputs(sum(lens), H, D, D, "bf16", seed)
+        cu = i32(np.concatenate([[0], np.cumsum(lens)]))
+        dev = {n: toks[n].to(DEV) for n in "qkvgb"}
+        pool = make_pool(4, H, D, D, "f32")
+        ws = torch.empty(kda.prefill_workspace_bytes(len(lens), sum(lens), H, D, D, C, torch.bfloat16),
+                         dtype=torch.uint8, device=DEV)
+        return dev, cu, pool, ws, len(lens)
+    calls = [setup(51, [700, 333]), setup(52, [1030])]
+    vt = {n: x.to(DEV) for n, x in wl.token_inputs(16 * 8, H, D, D, "bf16", 53, shape_prefix=(16, 8)).items()}
+    vpool = make_pool(16, H, D, D, "f32")
+    for s_ in range(16):
+        vpool[s_] = wl.pool_state(s_, H, D, D, "f32", 53).to(DEV)
+    ck = i32(list(range(16)))
+
+    def run_all(streams):
+        outs = []
+        for _, _, pool, _, _ in calls:
+            pool.fill_(0.0)
+        torch.cuda.synchronize()   # the pools are clear before any stream starts
+        for (dev, cu, pool, ws, n), st in zip(calls, streams[:2]):
+            with torch.cuda.stream(st):
+                o = kda.chunk_prefill(dev["q"], dev["k"], dev["v"], dev["g"], dev["b"], cu, C, pool,
+                                      i32([-1] * n), i32(list(range(n))), workspace=ws)
+            outs.append((o, pool))
+        with torch.cuda.stream(streams[2]):
+            vo = kda.recurrent_verify(vt["q"], vt["k"], vt["v"], vt["g"], vt["b"], vpool, ck)
+        torch.cuda.synchronize()
+        return [(o.clone(), p.clone()) for o, p in outs], [x.clone() for x in vo]
+
+    cur = torch.cuda.current_stream()
+    serial = run_all([cur, cur, cur])
+    side = [torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        conc = run_all(side)
+        for (o1, p1), (o2, p2) in zip(serial[0], conc[0]):
+            assert torch.equal(o1, o2) and torch.equal(p1, p2)
+        for a, b in zip(serial[1], conc[1]):
+            assert torch.equal(a, b)
 
 
 def test_graph_capture_replay():
