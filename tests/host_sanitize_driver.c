@@ -33,6 +33,10 @@ int main(void) {
   expect("workspace ok", kda_chunk_prefill_workspace(16, 135168, 32, 128, 128, 64, KDA_BF16, &ws), KDA_OK);
   if (ws == 0) { fprintf(stderr, "workspace size 0\n"); ++failures; }
   expect("workspace bad shape", kda_chunk_prefill_workspace(1, 64, 2, 32, 32, 16, KDA_BF16, &ws), KDA_ERR_UNSUPPORTED);
+  expect("workspace grid beyond range", kda_chunk_prefill_workspace(1, INT32_MAX, 129, 128, 128, 64, KDA_BF16, &ws),
+         KDA_ERR_UNSUPPORTED);
+  expect("workspace scan grid beyond range", kda_chunk_prefill_workspace(1 << 20, 64, 256, 128, 128, 64, KDA_BF16, &ws),
+         KDA_ERR_UNSUPPORTED);
 
   /* prefill */
 #define PREFILL(q, n_seqs, dk, chunk, in_dt, flags, wsb) \
