@@ -36,6 +36,10 @@ struct CommitSmem {
 //   c_t = k_t * prod_{t<s<to} alpha_s,
 // accumulated in reverse order with a running decay, positions staged in
 // LDS kBlk at a time.  Uniform across the workgroup (it holds barriers).
+// The records are read once, with non-temporal loads: in the decoding
+// loop's order (verify writes them, commit reads them, the next verify
+// rewrites them) that took commit from ~162.5 to 158.9 us, and the commit
+// right after a verify in the bench step from ~164 to 160 us.
 template <typename TRec>
 __device__ __forceinline__ void advance(floatx4 (&S)[kRows], int from, int to, const TRec* __restrict__ kg_rec,
                                         const float* __restrict__ u_rec, int64_t rec0, CommitSmem& sm) {
@@ -54,14 +58,14 @@ __device__ __forceinline__ void advance(floatx4 (&S)[kRows], int from, int to, c
       float dec = sm.dec[tid];
       for (int t = hi - 1; t >= lo; --t) {
         const TRec* kg = kg_rec + (rec0 + t) * (2 * kD);
-        sm.c[t - lo][tid] = dec * to_f32(kg[tid]);
-        dec *= __expf(to_f32(kg[kD + tid]));
+        sm.c[t - lo][tid] = dec * to_f32(__builtin_nontemporal_load(&kg[tid]));
+        dec *= __expf(to_f32(__builtin_nontemporal_load(&kg[kD + tid])));
       }
       sm.dec[tid] = dec;
     }
     for (int e = tid; e < cnt * kD; e += kT) {
       const int t = e / kD, vv = e % kD;
-      sm.u[t][vv] = u_rec[(rec0 + lo + t) * kD + vv];
+      sm.u[t][vv] = __builtin_nontemporal_load(&u_rec[(rec0 + lo + t) * kD + vv]);
     }
     __syncthreads();
     for (int t = 0; t < cnt; ++t) {
