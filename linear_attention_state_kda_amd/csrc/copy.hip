@@ -17,23 +17,34 @@ constexpr int kT = 256;
 constexpr int kVec = 4;                   // 16-byte vectors per thread per block
 constexpr int64_t kBlockBytes = kT * kVec * 16;
 
+// Pairs that share a source (a fork: one checkpoint to several children)
+// are copied by the blocks of the group's first valid pair: each part of
+// the source is read once and written to every destination of the group.
 __global__ __launch_bounds__(kT) void kda_copy_kernel(uint8_t* __restrict__ pool, int64_t n_slots,
                                                       int64_t slot_bytes, int blocks_per_pair,
                                                       const int32_t* __restrict__ src_slot,
                                                       const int32_t* __restrict__ dst_slot,
                                                       int n_pairs, int32_t* __restrict__ dev_err) {
+  __shared__ int s_dst[kT];
+  __shared__ int s_n, s_follower;
   const int pair = blockIdx.x / blocks_per_pair;
   const int part = blockIdx.x % blocks_per_pair;
   if (pair >= n_pairs) return;
+  auto slot_ok = [&](int x) { return x >= 0 && (int64_t)x < n_slots; };
   const int s = src_slot[pair], d = dst_slot[pair];
-  if (s < 0 || (int64_t)s >= n_slots || d < 0 || (int64_t)d >= n_slots) {
+  if (!slot_ok(s) || !slot_ok(d)) {
     if (part == 0 && threadIdx.x == 0) set_err(dev_err, 1u);
     return;
   }
-  if (s == d) return;
+  // an earlier valid pair with the same source leads the group
+  if (threadIdx.x == 0) s_follower = 0;
+  __syncthreads();
+  for (int q = threadIdx.x; q < pair; q += kT)
+    if (src_slot[q] == s && slot_ok(dst_slot[q])) s_follower = 1;
+  __syncthreads();
+  if (s_follower) return;
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   const u32x4* sp = reinterpret_cast<const u32x4*>(pool + (int64_t)s * slot_bytes);
-  u32x4* dp = reinterpret_cast<u32x4*>(pool + (int64_t)d * slot_bytes);
   const int64_t n16 = slot_bytes / 16;
   const int64_t base = (int64_t)part * (kT * kVec) + threadIdx.x;
   u32x4 buf[kVec];
@@ -42,10 +53,27 @@ __global__ __launch_bounds__(kT) void kda_copy_kernel(uint8_t* __restrict__ pool
     const int64_t e = base + (int64_t)i * kT;
     if (e < n16) buf[i] = __builtin_nontemporal_load(sp + e);
   }
+  // the group's destinations, kT pairs of the list at a time (a pair whose
+  // destination is its source is a no-op)
+  for (int q0 = pair; q0 < n_pairs; q0 += kT) {
+    if (threadIdx.x == 0) s_n = 0;
+    __syncthreads();
+    const int q = q0 + threadIdx.x;
+    if (q < n_pairs && src_slot[q] == s) {
+      const int dq = dst_slot[q];
+      if (slot_ok(dq) && dq != s) s_dst[atomicAdd(&s_n, 1)] = dq;
+    }
+    __syncthreads();
+    const int n = s_n;
+    for (int j = 0; j < n; ++j) {
+      u32x4* dp = reinterpret_cast<u32x4*>(pool + (int64_t)s_dst[j] * slot_bytes);
 #pragma unroll
-  for (int i = 0; i < kVec; ++i) {
-    const int64_t e = base + (int64_t)i * kT;
-    if (e < n16) __builtin_nontemporal_store(buf[i], dp + e);
+      for (int i = 0; i < kVec; ++i) {
+        const int64_t e = base + (int64_t)i * kT;
+        if (e < n16) __builtin_nontemporal_store(buf[i], dp + e);
+      }
+    }
+    __syncthreads();   // every thread has read s_n and s_dst before the next batch resets them
   }
 }
 

@@ -72,6 +72,30 @@ def test_copy_edge_cases():
     torch.cuda.synchronize()
 
 
+def test_copy_groups_sharing_a_source():
+    """Pairs that share a source are written by the group's first valid
+    pair: interleaved groups, a no-op pair (dst == src) leading its group,
+    an invalid destination inside a group and an invalid source (both
+    flagged and skipped), and one source forked to 300 children (more than
+    one batch of the group's destination list)."""
+    n_slots = 420
+    pool = make_pool(n_slots, 2, 128, 128, "f32")
+    host = fill_slots(pool, [3, 5, 7, 20], "f32", 9)
+    src = [5, 7, 5, 5, 430, 7, 5, 3, 3] + [20] * 300
+    dst = [10, 11, 5, 12, 13, 14, 999, 15, 16] + list(range(100, 400))
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kda.state_copy(pool, i32(src), i32(dst), dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() & kda.DEV_ERR_SLOT
+    expect = {10: 5, 12: 5, 11: 7, 14: 7, 15: 3, 16: 3, **{d: 20 for d in range(100, 400)}}
+    for d, s_ in expect.items():
+        assert torch.equal(pool[d].cpu(), host[s_]), (d, s_)
+    for s_ in (3, 5, 7, 20):
+        assert torch.equal(pool[s_].cpu(), host[s_])
+    written = set(expect) | {3, 5, 7, 20}
+    assert untouched(pool, sorted(set(range(n_slots)) - written), "f32")
+
+
 # ---------------------------------------------------------------- verify
 
 def run_verify_case(n_req, L, H, in_dtype, pool_dtype, seed):
