@@ -251,8 +251,8 @@ def measured_prefill_traffic():
 
 def committed_copy_traffic_ratio():
     """HBM bytes over algorithmic bytes of the fork copy, from the committed
-    FETCH_SIZE / WRITE_SIZE profile (the copy's sources are read once per
-    child, the repeats hitting the memory-side cache), or None if absent."""
+    FETCH_SIZE / WRITE_SIZE profile (the copy reads each shared source once
+    for all of its children), or None if absent."""
     try:
         for line in open(os.path.join(ROOT, "profiles", "state_paths_traffic.md")):
             if line.startswith("| copy"):

@@ -20,6 +20,10 @@ constexpr int64_t kBlockBytes = kT * kVec * 16;
 // Pairs that share a source (a fork: one checkpoint to several children)
 // are copied by the blocks of the group's first valid pair: each part of
 // the source is read once and written to every destination of the group.
+// Groups are formed within windows of kT consecutive pairs, so a block looks
+// at no more than kT entries of the lists and the launch stays linear in
+// n_pairs; a source whose pairs fall in several windows is read once per
+// window.
 __global__ __launch_bounds__(kT) void kda_copy_kernel(uint8_t* __restrict__ pool, int64_t n_slots,
                                                       int64_t slot_bytes, int blocks_per_pair,
                                                       const int32_t* __restrict__ src_slot,
@@ -36,11 +40,16 @@ __global__ __launch_bounds__(kT) void kda_copy_kernel(uint8_t* __restrict__ pool
     if (part == 0 && threadIdx.x == 0) set_err(dev_err, 1u);
     return;
   }
-  // an earlier valid pair with the same source leads the group
-  if (threadIdx.x == 0) s_follower = 0;
+  const int w0 = pair / kT * kT, w1 = min(w0 + kT, n_pairs);   // this pair's window
+  // an earlier valid pair of the window with the same source leads the group
+  if (threadIdx.x == 0) {
+    s_follower = 0;
+    s_n = 0;
+  }
   __syncthreads();
-  for (int q = threadIdx.x; q < pair; q += kT)
-    if (src_slot[q] == s && slot_ok(dst_slot[q])) s_follower = 1;
+  const int q = w0 + threadIdx.x;
+  const int sq = q < w1 ? src_slot[q] : -1;
+  if (q < pair && sq == s && slot_ok(dst_slot[q])) s_follower = 1;
   __syncthreads();
   if (s_follower) return;
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -53,27 +62,21 @@ __global__ __launch_bounds__(kT) void kda_copy_kernel(uint8_t* __restrict__ pool
     const int64_t e = base + (int64_t)i * kT;
     if (e < n16) buf[i] = __builtin_nontemporal_load(sp + e);
   }
-  // the group's destinations, kT pairs of the list at a time (a pair whose
-  // destination is its source is a no-op)
-  for (int q0 = pair; q0 < n_pairs; q0 += kT) {
-    if (threadIdx.x == 0) s_n = 0;
-    __syncthreads();
-    const int q = q0 + threadIdx.x;
-    if (q < n_pairs && src_slot[q] == s) {
-      const int dq = dst_slot[q];
-      if (slot_ok(dq) && dq != s) s_dst[atomicAdd(&s_n, 1)] = dq;
-    }
-    __syncthreads();
-    const int n = s_n;
-    for (int j = 0; j < n; ++j) {
-      u32x4* dp = reinterpret_cast<u32x4*>(pool + (int64_t)s_dst[j] * slot_bytes);
+  // the group's destinations in the window (a pair whose destination is its
+  // source is a no-op)
+  if (q >= pair && sq == s) {
+    const int dq = dst_slot[q];
+    if (slot_ok(dq) && dq != s) s_dst[atomicAdd(&s_n, 1)] = dq;
+  }
+  __syncthreads();
+  const int n = s_n;
+  for (int j = 0; j < n; ++j) {
+    u32x4* dp = reinterpret_cast<u32x4*>(pool + (int64_t)s_dst[j] * slot_bytes);
 #pragma unroll
-      for (int i = 0; i < kVec; ++i) {
-        const int64_t e = base + (int64_t)i * kT;
-        if (e < n16) __builtin_nontemporal_store(buf[i], dp + e);
-      }
+    for (int i = 0; i < kVec; ++i) {
+      const int64_t e = base + (int64_t)i * kT;
+      if (e < n16) __builtin_nontemporal_store(buf[i], dp + e);
     }
-    __syncthreads();   // every thread has read s_n and s_dst before the next batch resets them
   }
 }
 

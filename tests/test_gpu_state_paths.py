@@ -76,24 +76,49 @@ def test_copy_groups_sharing_a_source():
     """Pairs that share a source are written by the group's first valid
     pair: interleaved groups, a no-op pair (dst == src) leading its group,
     an invalid destination inside a group and an invalid source (both
-    flagged and skipped), and one source forked to 300 children (more than
-    one batch of the group's destination list)."""
+    flagged and skipped), and one source forked to 300 children, whose
+    pairs span two windows of 256 pairs, the first pair of the second
+    window having an invalid destination."""
     n_slots = 420
     pool = make_pool(n_slots, 2, 128, 128, "f32")
     host = fill_slots(pool, [3, 5, 7, 20], "f32", 9)
     src = [5, 7, 5, 5, 430, 7, 5, 3, 3] + [20] * 300
     dst = [10, 11, 5, 12, 13, 14, 999, 15, 16] + list(range(100, 400))
+    assert dst[256] == 347
+    dst[256] = 1000
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     kda.state_copy(pool, i32(src), i32(dst), dev_err=err)
     torch.cuda.synchronize()
     assert err.item() & kda.DEV_ERR_SLOT
-    expect = {10: 5, 12: 5, 11: 7, 14: 7, 15: 3, 16: 3, **{d: 20 for d in range(100, 400)}}
+    expect = {10: 5, 12: 5, 11: 7, 14: 7, 15: 3, 16: 3, **{d: 20 for d in range(100, 400) if d != 347}}
     for d, s_ in expect.items():
         assert torch.equal(pool[d].cpu(), host[s_]), (d, s_)
     for s_ in (3, 5, 7, 20):
         assert torch.equal(pool[s_].cpu(), host[s_])
     written = set(expect) | {3, 5, 7, 20}
     assert untouched(pool, sorted(set(range(n_slots)) - written), "f32")
+
+
+def test_copy_groups_across_windows():
+    """1,100 pairs over 37 sources, each source's children spread over all
+    five windows of 256 pairs (and over several places inside each): every
+    destination receives its source's bits and the sources stay unchanged."""
+    n_src, n_pairs = 37, 1100
+    n_slots = n_src + n_pairs
+    pool = make_pool(n_slots, 2, 128, 128, "bf16")
+    host = fill_slots(pool, list(range(n_src)), "bf16", 11)
+    src = [i % n_src for i in range(n_pairs)]
+    dst = [n_src + (i * 7) % n_pairs for i in range(n_pairs)]   # a permutation of the child slots
+    assert len(set(dst)) == n_pairs
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kda.state_copy(pool, i32(src), i32(dst), dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    out = pool.cpu()
+    for s_, d in zip(src, dst):
+        assert torch.equal(out[d], host[s_]), (s_, d)
+    for s_ in range(n_src):
+        assert torch.equal(out[s_], host[s_])
 
 
 # ---------------------------------------------------------------- verify
