@@ -42,6 +42,12 @@
  *    malformed cu_seqlens or track_ptr) set a bit in *dev_err (when dev_err
  *    is non-NULL, via atomic OR) and the offending item is skipped.  The
  *    caller clears *dev_err before the call if it wants a fresh word.
+ *  - A dispatch holds at most 2^32 - 1 work-items, so each call bounds its
+ *    launch grid on the host (KDA_ERR_UNSUPPORTED beyond it): prefill as
+ *    stated there; verify n_req * H, rounded up to a multiple of 8,
+ *    <= 8,388,607; commit and align commit n_req * H <= 16,777,215; copy
+ *    ceil(slot bytes / 16 KiB) * n_pairs <= 16,777,215; conv update
+ *    n_ops * n_tensors <= 16,777,215.
  *  - Every cast into a 16-bit output or pool is one round-to-nearest-even
  *    cast from an fp32 value held in registers.
  *  - Floating-point results are deterministic run to run.
@@ -137,8 +143,9 @@ kda_status kda_chunk_prefill_workspace(int32_t n_seqs, int64_t total_tokens, int
  * q, k, v, g, b   inputs in `in_dtype` (layouts above); o output, same dtype.
  * cu_seqlens      int32 [n_seqs + 1] token offsets, non-decreasing, last <= total_tokens.
  * sizes           total_tokens <= INT32_MAX, (total_tokens / chunk + n_seqs) * H
- *                 <= UINT32_MAX and n_seqs * H * 8 <= INT32_MAX (the launch
- *                 grids' index range), else KDA_ERR_UNSUPPORTED.
+ *                 <= 16,777,215 and n_seqs * H, rounded up to a multiple of
+ *                 8, <= 2,097,151 (the launch grids' work-item limit, see
+ *                 the conventions), else KDA_ERR_UNSUPPORTED.
  * pool            state pool; pool.H, d_k, d_v must equal H, d_k, d_v.
  * init_slot       int32 [n_seqs]: slot holding the initial state of sequence
  *                 i (upcast exactly to fp32), or -1 for a zero state.

@@ -12,6 +12,24 @@
 
 namespace {
 
+// A dispatch carries its size in work-items in a 32-bit field, so a launch
+// of `blocks` workgroups of `threads` work-items must keep the product
+// within 2^32 - 1.  The work-items per unit of each call, from its kernels:
+// the prefill's prep 256 per (chunk slot, head), its scan at most 2,048 per
+// (sequence, head) pair, the pairs rounded up to a multiple of 8 (the
+// general form: d_v / 16 <= 8 tiles of 256; the 16-bit form: 1,152 once
+// more than 64 pairs, fewer pairs giving a grid far below the limit);
+// verify 512 per
+// (request, head), the items rounded up to a multiple of 8; commit and
+// align commit 256 per (request, head); copy 256 per 16 KiB of a slot per
+// pair; the conv update 256 per (op, tensor).
+bool grid_fits(int64_t blocks, int64_t threads) { return blocks <= (int64_t)UINT32_MAX / threads; }
+int64_t up8(int64_t x) { return (x + 7) / 8 * 8; }
+bool prefill_grids_fit(int64_t total_tokens, int32_t n_seqs, int32_t H, int32_t chunk) {
+  return grid_fits((total_tokens / chunk + n_seqs) * (int64_t)H, 256) &&
+         grid_fits(up8((int64_t)n_seqs * H), 2048);
+}
+
 bool dtype_ok(int32_t dt) { return dt == KDA_F32 || dt == KDA_F16 || dt == KDA_BF16; }
 
 size_t dtype_size(int32_t dt) { return dt == KDA_F32 ? 4 : 2; }
@@ -56,8 +74,7 @@ kda_status kda_chunk_prefill_workspace(int32_t n_seqs, int64_t total_tokens, int
   if (!dtype_ok(in_dtype)) return KDA_ERR_UNSUPPORTED;
   if (!kda::prefill_supported(d_k, d_v, chunk, in_dtype, KDA_F32)) return KDA_ERR_UNSUPPORTED;
   if (total_tokens > INT32_MAX) return KDA_ERR_UNSUPPORTED;
-  if ((total_tokens / chunk + n_seqs) * (int64_t)H > UINT32_MAX || (int64_t)n_seqs * H * 8 > INT32_MAX)
-    return KDA_ERR_UNSUPPORTED;
+  if (!prefill_grids_fit(total_tokens, n_seqs, H, chunk)) return KDA_ERR_UNSUPPORTED;
   *bytes = kda::prefill_workspace_bytes(n_seqs, total_tokens, H, d_k, d_v, chunk, in_dtype);
   return KDA_OK;
 }
@@ -80,10 +97,7 @@ kda_status prefill_check(const void* q, const void* k, const void* v, const void
   if (!dtype_ok(in_dtype)) return KDA_ERR_UNSUPPORTED;
   if (!kda::prefill_supported(d_k, d_v, chunk, in_dtype, pool.dtype)) return KDA_ERR_UNSUPPORTED;
   if (total_tokens > INT32_MAX) return KDA_ERR_UNSUPPORTED;
-  // launch grids: one workgroup per (chunk slot, head) for the prep, up to
-  // eight per (sequence, head) for the scan
-  if ((total_tokens / chunk + n_seqs) * (int64_t)H > UINT32_MAX || (int64_t)n_seqs * H * 8 > INT32_MAX)
-    return KDA_ERR_UNSUPPORTED;
+  if (!prefill_grids_fit(total_tokens, n_seqs, H, chunk)) return KDA_ERR_UNSUPPORTED;
   kda_status ps = check_pool(pool, H, d_k, d_v);
   if (ps != KDA_OK) return ps;
   if (n_seqs == 0) return KDA_OK;
@@ -181,7 +195,7 @@ kda_status kda_recurrent_verify(const void* q, const void* k, const void* v, con
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16) || !aligned(o, 16) ||
       !aligned(u_rec, 16) || !aligned(kg_rec, 16))
     return KDA_ERR_INVALID_ARG;
-  if ((int64_t)n_req * H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  if (!grid_fits(up8((int64_t)n_req * H), 512)) return KDA_ERR_UNSUPPORTED;
   kda::VerifyArgs a{q, k, v, g, b, o, in_dtype, n_req, L, H, d_k, pool_desc(pool), ckpt_slot,
                     u_rec, kg_rec, dev_err, flags};
   return launched(kda::launch_verify(a, static_cast<hipStream_t>(stream)));
@@ -200,7 +214,7 @@ kda_status kda_commit(kda_pool pool, const int32_t* ckpt_slot, const int32_t* ds
   if (n_req == 0) return KDA_OK;
   if (ckpt_slot == nullptr || accepted_len == nullptr || u_rec == nullptr || kg_rec == nullptr)
     return KDA_ERR_INVALID_ARG;
-  if ((int64_t)n_req * H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  if (!grid_fits((int64_t)n_req * H, 256)) return KDA_ERR_UNSUPPORTED;
   kda::CommitArgs a{pool_desc(pool), ckpt_slot, dst_slot, accepted_len, u_rec, kg_rec, rec_dtype,
                     n_req, L, H, d_k, dev_err};
   return launched(kda::launch_commit(a, static_cast<hipStream_t>(stream)));
@@ -222,7 +236,7 @@ kda_status kda_commit_align(kda_pool pool, const int32_t* block_table, int32_t b
   if (block_table == nullptr || num_tokens == nullptr || accepted_len == nullptr || u_rec == nullptr ||
       kg_rec == nullptr)
     return KDA_ERR_INVALID_ARG;
-  if ((int64_t)n_req * H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  if (!grid_fits((int64_t)n_req * H, 256)) return KDA_ERR_UNSUPPORTED;
   kda::CommitAlignArgs a{pool_desc(pool), block_table, blocks_per_req, num_tokens, accepted_len, block_size,
                          u_rec, kg_rec, rec_dtype, n_req, L, H, d_k, next.num_tokens, next.block,
                          next.ckpt_slot, next.copy_bias, dev_err};
@@ -241,7 +255,7 @@ kda_status kda_state_copy(kda_pool pool, const int32_t* src_slot, const int32_t*
   if (n_pairs == 0) return KDA_OK;
   if (src_slot == nullptr || dst_slot == nullptr) return KDA_ERR_INVALID_ARG;
   const int64_t bpp = (slot_bytes + 16383) / 16384;
-  if (bpp * n_pairs > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  if (!grid_fits(bpp * n_pairs, 256)) return KDA_ERR_UNSUPPORTED;
   kda::CopyArgs a{pool_desc(pool), src_slot, dst_slot, n_pairs, slot_bytes, dev_err};
   return launched(kda::launch_copy(a, static_cast<hipStream_t>(stream)));
 }
@@ -275,7 +289,7 @@ kda_status kda_conv_state_update(const kda_conv_tensor* tensors, int32_t n_tenso
   }
   if (n_ops == 0) return KDA_OK;
   if (dst_slot == nullptr || src_slot == nullptr || shift == nullptr) return KDA_ERR_INVALID_ARG;
-  if ((int64_t)n_ops * n_tensors > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  if (!grid_fits((int64_t)n_ops * n_tensors, 256)) return KDA_ERR_UNSUPPORTED;
   a.dst_slot = dst_slot;
   a.src_slot = src_slot;
   a.shift = shift;

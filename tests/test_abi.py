@@ -85,7 +85,7 @@ def test_prefill_host_errors(L):
     for name in ("q", "k", "v", "g", "o", "tf32"):   # every vector-accessed buffer must be 16-byte aligned
         assert prefill(L, **{name: ctypes.c_void_p(0x1008)}) == 1, name
     assert prefill(L, T=1 << 33) == 2
-    # launch grids beyond their index range: (chunk slots x heads) and (sequences x heads x 8)
+    # launch grids beyond the work-item limit (more in test_launch_grid_limits)
     assert prefill(L, T=(1 << 31) - 1, H=129, pool=pool(H=129)) == 2
     assert prefill(L, n_seqs=1 << 20, H=256, pool=pool(H=256)) == 2
     assert prefill(L, flags=2) == 1             # unknown flag bit
@@ -182,6 +182,39 @@ def test_conv_state_update_host_errors(L):
     assert call([conv_tensor(dim=4100, stride=11 * 4100 * 2 + 8)], n=0) == 2   # row not 16-byte units
     assert call([good], dst=None) == 1
     assert call([good], sh=None) == 1
+
+
+def test_launch_grid_limits(L):
+    """A dispatch holds at most 2^32 - 1 work-items: each call rejects, on the
+    host, sizes whose grid would not fit (KDA_ERR_UNSUPPORTED), at the bounds
+    include/kda.h states.  A prefill just inside its bounds passes the grid
+    check and stops at the workspace check instead (nothing is launched; the
+    other calls have no later host check, so only their far side is run)."""
+    lim = 0xFFFFFFFF
+    # prefill prep: (T / 64 + n_seqs) * H workgroups of 256
+    inside = 64 * (lim // 256 // 2 - 1)
+    assert (inside // 64 + 1) * 2 * 256 <= lim < (inside // 64 + 2) * 2 * 256
+    assert prefill(L, T=inside, ws_bytes=16) == 3
+    assert prefill(L, T=inside + 64, ws_bytes=16) == 2
+    # prefill scan: n_seqs * H, rounded up to 8, times 2,048
+    n_in = (lim // 2048) // 8 * 8 // 2
+    assert prefill(L, n_seqs=n_in, ws_bytes=16) == 3
+    assert prefill(L, n_seqs=n_in + 1, ws_bytes=16) == 2
+    assert L.kda_chunk_prefill_workspace(n_in + 1, 100, 2, 128, 128, 64, 2, ctypes.byref(ctypes.c_size_t())) == 2
+    P = pool()
+    # verify: 512 work-items per (request, head), rounded up to 8 items
+    assert L.kda_recurrent_verify(FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, lim // 512 // 2 + 1, 8, 2, 128,
+                                  128, P, FAKE, FAKE, FAKE, 0, None, None) == 2
+    # commit and align commit: 256 per (request, head)
+    n_c = lim // 256 // 2 + 1
+    assert L.kda_commit(P, FAKE, None, FAKE, FAKE, FAKE, 2, n_c, 8, 2, 128, 128, None, None) == 2
+    assert L.kda_commit_align(P, FAKE, 4, FAKE, FAKE, 64, FAKE, FAKE, 2, n_c, 8, 2, 128, 128,
+                              kda.KdaAlignNext(None, None, None, None), None, None) == 2
+    # copy: 256 per 16 KiB of a slot per pair (fp32 slots of 2 x 128 x 128: 8 blocks per pair)
+    assert L.kda_state_copy(P, FAKE, FAKE, lim // 256 // 8 + 1, None, None) == 2
+    # conv update: 256 per (op, tensor)
+    arr = (kda.KdaConvTensor * 2)(conv_tensor(), conv_tensor())
+    assert L.kda_conv_state_update(arr, 2, FAKE, FAKE, FAKE, lim // 256 // 2 + 1, None, None) == 2
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
