@@ -509,10 +509,10 @@ def main():
         "copy_hbm_traffic": None if copy_ratio is None else {
             "GBps": gbs["copy"] * copy_ratio, "hbm_frac": gbs["copy"] * copy_ratio * 1e9 / HBM_PEAK,
             "ratio": copy_ratio,
-            "note": "the copy's algorithmic bytes charge every pair a full source read; its 64 sources are "
-                    "read once per child and the repeats hit the memory-side cache, so its HBM traffic is "
-                    "this ratio of the algorithmic bytes (profiles/state_paths_traffic.md, rocprofv3 "
-                    "FETCH_SIZE + WRITE_SIZE; not measured in this run)"},
+            "note": "the copy's algorithmic bytes charge every pair a full source read; the kernel reads "
+                    "each of the 64 sources once for its four children, so its HBM traffic is this ratio "
+                    "of the algorithmic bytes (profiles/state_paths_traffic.md, rocprofv3 FETCH_SIZE + "
+                    "WRITE_SIZE; not measured in this run)"},
         "hbm_reference": hbm_reference,
         "cold": None if cold is None else {
             "note": "L2 and MALL flushed by a 512 MiB write and the checkpoints restored before each step",
