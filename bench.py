@@ -309,12 +309,17 @@ def cpu_baseline(case, seconds_target=20.0):
         t_probe = max(ex.map(_oracle_heads, [(case, g, probe) for g in groups]))
         n = int(max(256, min(case["lengths"][0], probe * seconds_target / max(t_probe, 1e-6))))
         t0 = time.perf_counter()
-        worst = max(ex.map(_oracle_heads, [(case, g, n) for g in groups]))
+        times = list(ex.map(_oracle_heads, [(case, g, n) for g in groups]))
         wall = time.perf_counter() - t0
+    worst = max(times)
+    # one core's rate on the whole workload: each process's seconds per head, averaged, times H
+    per_head = float(np.mean([t / len(g) for t, g in zip(times, groups)]))
     return {"value": n / worst, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "single_core_value": n / (per_head * H),
             "sample": f"first {n} of {case['lengths'][0]} tokens of the single-layer prefill, all {H} heads "
                       f"in {cores} processes of {H // cores}-{-(-H // cores)} heads each, fp64 token loop "
-                      f"(slowest process {worst:.1f} s, {wall:.1f} s wall with input setup)"}
+                      f"(slowest process {worst:.1f} s, {wall:.1f} s wall with input setup); "
+                      f"single_core_value: all {H} heads on one core, from the processes' mean time per head"}
 
 
 def main():

@@ -52,6 +52,7 @@ def test_cpu_baseline_times_a_bounded_sample():
     want = min(len(os.sched_getaffinity(0)), 16, 32)
     assert cb["kind"] == "oracle" and cb["cores"] == want and cb["unit"] == "tokens/s"
     assert cb["value"] > 0
+    assert 0 < cb["single_core_value"] <= cb["value"] * 1.2   # one core is no faster than all of them
     assert cb["sample"].startswith("first 256 of 8229 tokens")
 
 
@@ -64,9 +65,10 @@ def test_head_subset_draw_matches_full_draw():
 
 def test_copy_traffic_ratio_is_read_from_the_committed_profile():
     """The fork copy's HBM-traffic ratio comes from the committed counter
-    summary: its 64 sources are read once per child, so the ratio lies
-    between the one-read-per-source floor (0.625 of the algorithmic bytes:
-    64 of 256 source reads plus all 256 writes) and 1."""
+    summary: the kernel reads each of its 64 sources once for its four
+    children, so the ratio sits at the one-read-per-source floor (0.625 of
+    the algorithmic bytes: 64 of 256 source reads plus all 256 writes),
+    within counter noise."""
     import bench
     r = bench.committed_copy_traffic_ratio()
-    assert r is not None and 0.62 <= r <= 1.0
+    assert r is not None and 0.62 <= r <= 0.65
