@@ -26,7 +26,7 @@ oracle on the host's cores (one process per group of heads), before the GPU
 is touched.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-varlen]
-       python bench.py --only-leg long|varlen   (one informational leg alone, for profiling)
+       python bench.py --only-leg long|varlen|graph   (one informational leg alone, for profiling)
 """
 
 import argparse
@@ -82,8 +82,8 @@ def prefill_setup(dev):
     return case, args, T, bytes_, flops
 
 
-def spec_setup(dev):
-    case = wl.spec_case(seed=3)
+def spec_setup(dev, **sizes):
+    case = wl.spec_case(seed=3, **sizes)
     n_req, L, H, d = case["n_req"], case["L"], case["H"], case["dk"]
     toks = wl.token_inputs(n_req * L, H, d, d, "bf16", case["seed"], shape_prefix=(n_req, L))
     t = {n: toks[n].to(dev) for n in "qkvgb"}
@@ -225,6 +225,60 @@ def decode_loop_leg(sp, st, iters=10, warm=3):
     return out
 
 
+def graph_loop_leg(dev, batches=(4, 16, 64), iters=200, warm=100):
+    """The decoding loop (verify, in-place commit, fork copy) on small
+    batches, where each kernel lasts a few microseconds and submitting the
+    launches can cost as much as running them: back-to-back iterations
+    issued one call at a time against the same iteration captured once as a
+    HIP graph and replayed (every call is capturable: no allocation, no
+    memset, no host read-back).  Per-iteration time over `iters` iterations,
+    after `warm` untimed ones (fewer leave the first batch's eager loop
+    several times slower while the device ramps up)."""
+    return {"workload": f"verify -> commit -> fork copy, L=8, H=32, fp32 pool, fork of n_req/4 "
+                        f"checkpoints to 4 children each; {iters} iterations back to back",
+            "by_batch": [_graph_loop(dev, n, iters, warm) for n in batches]}
+
+
+def _graph_loop(dev, n_req, iters, warm):
+    sp = spec_setup(dev, n_req=n_req, n_slots=4 * n_req + 64, n_fork_src=n_req // 4)
+    t = sp["t"]
+
+    def one():
+        kda.recurrent_verify(t["q"], t["k"], t["v"], t["g"], t["b"], sp["pool"], sp["ckpt"],
+                             o=sp["o"], u_rec=sp["u_rec"], kg_rec=sp["kg_rec"])
+        kda.commit(sp["pool"], sp["ckpt"], sp["acc"], sp["u_rec"], sp["kg_rec"])
+        kda.state_copy(sp["pool"], sp["src"], sp["dst"])
+
+    def timed(run):
+        for _ in range(warm):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record()
+        for _ in range(iters):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters * 1e3, (time.perf_counter() - w0) / iters * 1e6
+
+    eager_us, eager_wall = timed(one)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        one()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        one()
+    graph_us, graph_wall = timed(g.replay)
+    nbytes = sum(sp["bytes"][c] for c in ("verify", "commit", "copy"))
+    return {"n_req": n_req, "eager_us_per_iter": round(eager_us, 2), "graph_us_per_iter": round(graph_us, 2),
+            "eager_host_us_per_iter": round(eager_wall, 2), "graph_host_us_per_iter": round(graph_wall, 2),
+            "hbm_frac_eager": round(nbytes / (eager_us * 1e-6) / HBM_PEAK, 4),
+            "hbm_frac_graph": round(nbytes / (graph_us * 1e-6) / HBM_PEAK, 4)}
+
+
 def measured_prefill_traffic():
     """HBM bytes per prefill call from the committed FETCH_SIZE / WRITE_SIZE
     profile (already scaled by the copy calibration), or None when the
@@ -333,9 +387,10 @@ def main():
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the informational legs (prefill on the varlen batch of 16 "
                          "sequences and on the long-context sequence of 131072 tokens; the "
-                         "speculative-decoding loop)")
-    ap.add_argument("--only-leg", choices=("long", "varlen"), default=None,
-                    help="run one informational prefill leg alone (10 timed calls) and print it")
+                         "speculative-decoding loop, eager and as a replayed HIP graph)")
+    ap.add_argument("--only-leg", choices=("long", "varlen", "graph"), default=None,
+                    help="run one informational leg alone and print it: a prefill leg (10 timed "
+                         "calls) or the small-batch decoding loop, eager and graph-replayed")
     ap.add_argument("--traffic-calibration", action="store_true",
                     help="after the timed steps, run one kda_state_copy of 256 distinct fp32 "
                          "slots (512 MiB read + 512 MiB written) so that FETCH_SIZE / WRITE_SIZE "
@@ -355,6 +410,9 @@ def main():
     dev = torch.device("cuda:0")
     kda.lib()
     st = torch.cuda.current_stream()
+    if a.only_leg == "graph":
+        print(json.dumps({"leg": a.only_leg, **graph_loop_leg(dev)}), flush=True)
+        return
     if a.only_leg is not None:
         leg = wl.long_prefill() if a.only_leg == "long" else wl.varlen_prefill("f32")
         print(json.dumps({"leg": a.only_leg, **time_leg(dev, st, leg, a.only_leg, reps=10)}), flush=True)
@@ -425,10 +483,13 @@ def main():
     # Informational legs, outside the step and `value`: the same prefill
     # kernels on the varlen batch, where 16 sequences give the scan 16x more
     # independent chains than the single-layer workload's one, and on the
-    # long-context sequence (2048 serial chunks, a snapshot every 64).
-    varlen = long_ctx = loop = None
+    # long-context sequence (2048 serial chunks, a snapshot every 64); the
+    # speculative-decoding loop in its own order, and on a small batch eager
+    # against a replayed HIP graph.
+    varlen = long_ctx = loop = graph_loop = None
     if not a.no_varlen:
         loop = decode_loop_leg(sp, st)
+        graph_loop = graph_loop_leg(dev)
         varlen = time_leg(dev, st, wl.varlen_prefill("f32"), "varlen prefill, pool initial states, "
                                                               "one snapshot per sequence")
         long_ctx = time_leg(dev, st, wl.long_prefill(), "long-context prefill, zero initial state, "
@@ -527,6 +588,7 @@ def main():
         "prefill_varlen": varlen,
         "prefill_long": long_ctx,
         "decode_loop": loop,
+        "decode_loop_graph": graph_loop,
         "device": torch.cuda.get_device_name(0),
     }
     if cb is not None:
