@@ -94,22 +94,21 @@ def lib():
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()   # ctypes passes the int as a c_void_p argument
 
 
 def _shape(t, name, shape):
     """Raise ValueError unless tensor ``t`` (if given) has exactly ``shape``.
     The C ABI sees raw pointers only, so every buffer size is checked here,
     before any call: an undersized output would be written out of bounds."""
-    if t is None:
-        return
-    if tuple(t.shape) != tuple(int(x) for x in shape):
+    if t is not None and t.shape != shape:   # torch.Size compares as a tuple
         raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)}, got {tuple(t.shape)}")
 
 
 def _same_device(ref, tensors):
+    want = ref.get_device()
     for name, t in tensors:
-        if t is not None and t.device != ref.device:
+        if t is not None and t.get_device() != want:
             raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
 
 
@@ -127,7 +126,7 @@ def _dev(t, name, dtype=None, ndim=None):
 
 
 def _stream():
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _pool(pool):
