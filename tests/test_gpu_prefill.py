@@ -332,3 +332,18 @@ def test_varlen_sampled_heads(pool_dtype):
                        label=f"varlen pool={pool_dtype} all heads of seqs {shortest} "
                              f"(lengths {[case['lengths'][i] for i in shortest]})")
     print("varlen", pool_dtype, "worst", w, w_all)
+
+
+def test_varlen_fp16_inputs():
+    """The varlen batch at full shape with fp16 inputs and an fp16 pool (the
+    64-column fp16 scan tiles): the oracle on heads 0 and 21 of every
+    sequence and on all 32 heads of the two shortest sequences, including
+    each snapshot's single rounding into the pool."""
+    case = wl.varlen_prefill(pool_dtype="f16", in_dtype="f16", seed=5)
+    toks, cu = tokens(case)
+    g = run_gpu(case, toks, cu)
+    w = check_case(case, toks, cu, g, [0, 21], label="varlen fp16 heads 0,21")
+    shortest = sorted(range(len(case["lengths"])), key=lambda i: case["lengths"][i])[:2]
+    w_all = check_case(case, toks, cu, g, list(range(case["H"])), check_untouched=False, seqs=shortest,
+                       label=f"varlen fp16 all heads of seqs {shortest}")
+    print("varlen fp16 worst", w, w_all)

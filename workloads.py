@@ -133,9 +133,9 @@ def single_layer_prefill(seed=1):
                         True, seed, "single-layer T=8229 H=32 d=128 C=64 bf16")
 
 
-def varlen_prefill(pool_dtype="f32", seed=2, n_seqs=16, H=32, lo=512, hi=16384, n_slots=1024):
+def varlen_prefill(pool_dtype="f32", seed=2, n_seqs=16, H=32, lo=512, hi=16384, n_slots=1024, in_dtype="bf16"):
     """16 packed sequences with lengths ~ U[512, 16384], H = 32, d = 128,
-    chunk 64, bf16 inputs; initial states from 16 distinct random slots of a
+    chunk 64, bf16 inputs (or in_dtype); initial states from 16 distinct random slots of a
     1024-slot pool; final states and one snapshot per sequence (chunk
     c_i ~ U{1..floor(T_i/64)}) to fresh slots, plus the fp32 snapshots."""
     lengths = _rng(seed, TAG_LEN).integers(lo, hi + 1, n_seqs)
@@ -143,8 +143,8 @@ def varlen_prefill(pool_dtype="f32", seed=2, n_seqs=16, H=32, lo=512, hi=16384, 
     init, final, trk = slots[:n_seqs], slots[n_seqs:2 * n_seqs], slots[2 * n_seqs:]
     cs = [int(_rng(seed, TAG_TRACK, i).integers(1, max(1, L // 64) + 1)) for i, L in enumerate(lengths)]
     tracks = [(i, cs[i], int(trk[i])) for i in range(n_seqs)]
-    return prefill_case(lengths, H, 128, 128, 64, "bf16", pool_dtype, n_slots, init, final,
-                        tracks, True, seed, f"varlen {n_seqs} seqs H={H} d=128 C=64 bf16 pool={pool_dtype}")
+    return prefill_case(lengths, H, 128, 128, 64, in_dtype, pool_dtype, n_slots, init, final,
+                        tracks, True, seed, f"varlen {n_seqs} seqs H={H} d=128 C=64 {in_dtype} pool={pool_dtype}")
 
 
 def long_prefill(seed=4, T=131072, H=32):
