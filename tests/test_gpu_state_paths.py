@@ -263,6 +263,43 @@ def test_commit_matches_oracle(pool_dtype, in_dtype):
     wr.check(f"commit pool={pool_dtype} in={in_dtype} vs replay")
 
 
+def test_verify_commit_full_shape_fp16():
+    """The speculative-decode shape (256 requests x 32 heads, L = 8) with fp16
+    inputs and an fp16 pool: verify's outputs at the fp16 bar, then every
+    committed state element within one fp16 ulp of the fp64 closed form plus
+    the fp32 arithmetic's own error (the commit accumulates at most L = 8
+    terms of the state's magnitude in fp32, ~2^-24 relative each, then rounds
+    once, to nearest even, into the pool: 1e-6 of the head's largest element
+    covers the fp32 part, which matters only for elements near zero, whose
+    fp16 ulp is as small as that error)."""
+    n_req, L, H, d = 256, 8, 32, 128
+    r = run_verify_case(n_req=n_req, L=L, H=H, in_dtype="f16", pool_dtype="f16", seed=8)
+    check_verify(r, "f16", "verify fp16 256 req x 32 heads L=8")
+    acc = wl.spec_case(seed=8)["accepted"]
+    pool, ckpt = r["pool"], r["ckpt"]
+    before = pool.clone()
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kda.commit(pool, i32(ckpt), i32(acc), r["u_rec"], r["kg_rec"], dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    u64 = r["u_rec"].cpu().double().numpy()
+    kg64 = wl.exact(r["kg_rec"].cpu())
+    worst = 0.0
+    for i in range(n_req):
+        s_ = int(ckpt[i])
+        if acc[i] == 0:
+            assert torch.equal(pool[s_], before[s_])
+            continue
+        ref = ko.commit_ref(r["S0"][i], kg64[i, :, :, :d], kg64[i, :, :, d:], u64[i], int(acc[i]))
+        got = to_math(pool[s_])
+        ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+        slack = 1e-6 * np.abs(ref).max(axis=(1, 2), keepdims=True)   # per head
+        excess = np.abs(got - ref) / (ulp + slack)
+        worst = max(worst, float(excess.max()))
+        assert excess.max() <= 1.0, (i, float(excess.max()))
+    print(f"[parity] commit fp16 pool 256 req x 32 heads: worst |got - ref| = {worst:.3f} of (fp16 ulp + fp32 slack)")
+
+
 def test_commit_to_other_slot_and_errors():
     n_req, L, H, d = 4, 8, 2, 128
     r = run_verify_case(n_req=n_req, L=L, H=H, in_dtype="bf16", pool_dtype="f32", seed=41)
