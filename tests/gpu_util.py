@@ -49,6 +49,28 @@ def to_math(pool_slot):
     return np.swapaxes(wl.exact(pool_slot.detach().cpu()), -1, -2)
 
 
+def ulp16(x, pool_dtype):
+    """Spacing of the 16-bit pool format at |x| (fp16: 10 stored mantissa
+    bits, subnormals from 2^-24; bf16: 7 bits): the distance between the two
+    representable values around x, so a once-rounded value lies within half
+    of it."""
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(ax)
+    bits, tiny = (10, 2.0 ** -24) if pool_dtype == "f16" else (7, 2.0 ** -133)
+    return np.where(ax == 0, tiny, np.maximum(np.ldexp(1.0, e - 1 - bits), tiny))
+
+
+def rounding_excess(got, ref, pool_dtype, slack_rel=1e-6):
+    """|got - ref| in units of (half a 16-bit ulp of ref + slack_rel of the
+    largest |ref| of the state): at most 1 for a state computed in fp32 from
+    exact operands and rounded once, to nearest, into the pool. The slack
+    covers the fp32 arithmetic's own error, which matters only for elements
+    near zero, whose 16-bit ulp is as small as that error."""
+    ref = np.asarray(ref, dtype=np.float64)
+    slack = slack_rel * np.abs(ref).max(axis=(-2, -1), keepdims=True)
+    return np.abs(np.asarray(got, dtype=np.float64) - ref) / (0.5 * ulp16(ref, pool_dtype) + slack)
+
+
 def rel(x, ref):
     nr = np.linalg.norm(ref)
     if nr == 0.0:
